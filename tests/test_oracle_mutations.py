@@ -1,0 +1,76 @@
+"""Planted-mistake check for the oracle's pins (CPU only).
+
+Each mutant is the oracle's C source with one plausible mistake (a wrong
+sign, a dropped term, an off-by-one, a wrong head index, ...). It is compiled
+to a temporary library and every pin in ``test_oracle_pins`` is run against
+it; at least one pin must fail. The mistakes are planted only in throw-away
+copies of the oracle, never in the product path.
+"""
+
+import math
+import os
+
+import pytest
+
+import oracle
+from tests import test_oracle_pins as pins
+
+SRC = open(os.path.join(os.path.dirname(oracle.__file__), "bsp_oracle.c")).read()
+
+MUTANTS = {
+    "gap_sign": [("gap = m[r] - mloc[r];", "gap = mloc[r] - m[r];")],
+    "non_strict": [("int skip = (mingap > lambda);", "int skip = (mingap >= lambda);")],
+    "no_acc_rescale": [("for (int d = 0; d < D; ++d) a[d] *= alpha;", "")],
+    "no_l_rescale": [("l[r] = alpha * l[r] + rowsum;", "l[r] = l[r] + rowsum;")],
+    "running_max_frozen": [("m[r] = mnew;", "")],
+    "causal_strict": [("if (c0 + c <= qi) {", "if (c0 + c < qi || (c0 + c == 0 && qi == 0)) {")],
+    "drop_diagonal_block": [("const int nblk = (r1 - 1) / block_k + 1;",
+                             "const int nblk = (r1 - 1) / block_k + ((r1 - 1) % block_k == block_k - 1);")],
+    "gqa_modulo": [("const int g = h / group;", "const int g = h % n_heads_kv;")],
+    "scale_wrong": [("const double scale = 1.0 / sqrt((double)head_dim);",
+                     "const double scale = 1.0 / (double)head_dim;")],
+    "lse_log2": [("lse_w[r] = m[r] + log(l[r]);", "lse_w[r] = m[r] + log2(l[r]);")],
+    "any_row_rule": [("double mingap = INFINITY;", "double mingap = -INFINITY;"),
+                     ("if (gap < mingap) mingap = gap;", "if (gap > mingap) mingap = gap;")],
+    "masked_row_blocks": [("gap = INFINITY;             /* nothing visible in this block */",
+                           "gap = -INFINITY;")],
+    "k_scale_ignored": [("const double sk = k_scale ? k_scale[g] : 1.0;", "const double sk = 1.0;")],
+    "v_offset": [("(double)v[((size_t)(base + c0 + c) * n_heads_kv + g) * D + d] * sv;",
+                  "(double)v[((size_t)(base + c0 + (c + 1) % nc) * n_heads_kv + g) * D + d] * sv;")],
+}
+
+
+def _pin_calls():
+    """Every pin test as a zero-argument callable (parametrisations expanded)."""
+    calls = []
+    for case in pins.CASES:
+        calls.append(lambda c=case: pins.test_dense_limit_equals_naive_softmax(c))
+        for lam in [0.0, 2.0]:
+            calls.append(lambda c=case, l=lam: pins.test_skip_set_matches_brute_force(c, l))
+            calls.append(lambda c=case, l=lam: pins.test_kept_key_closed_form(c, l))
+    for lam in [0.0, math.inf]:
+        calls.append(lambda l=lam: pins.test_probabilities_sum_to_one_and_reproduce_output(l))
+    calls += [pins.test_block_zero_never_skipped_and_output_finite,
+              pins.test_golden_worked_examples,
+              pins.test_tie_at_lambda_is_kept_on_random_integer_scores,
+              pins.test_fp8_scales_are_applied_per_head,
+              pins.test_gqa_equals_repeated_mha]
+    return calls
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path, monkeypatch):
+    src = SRC
+    for old, new in MUTANTS[name]:
+        assert old in src, f"mutation anchor for {name} not found"
+        src = src.replace(old, new)
+    lib = oracle.load_library(oracle.compile_source(src, str(tmp_path / f"mut_{name}.so")))
+    monkeypatch.setattr(oracle, "_lib", lib)
+    failed = 0
+    for call in _pin_calls():
+        try:
+            call()
+        except (AssertionError, ValueError, FloatingPointError):
+            failed += 1
+            break
+    assert failed > 0, f"no pin detects mutant {name}"
