@@ -1,0 +1,192 @@
+"""Python binding of ``libbsp_attn.so`` (causal block-sparse prefill attention
+with dynamic block skipping, MI355X / gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/bsp_attn.h``. PyTorch supplies
+device memory and the current stream. There is no fallback: when the library
+is missing or the device is not gfx950 the calls raise.
+
+Method: page "长上下文推理加速方案部署实战：基于动态稀疏注意力机制的推理服务优化指南"
+(deployment guide for a dynamic sparse attention kernel), sections 3.2, 3.3,
+3.5 and 5 (steps 3 and 4).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch  # must be imported before the library so both share one HIP runtime
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libbsp_attn.so")
+
+BSP_OK, BSP_ERR_INVALID_ARG, BSP_ERR_UNSUPPORTED, BSP_ERR_HIP, BSP_ERR_DEVICE = range(5)
+BSP_F32, BSP_BF16, BSP_FP8_E4M3 = 0, 1, 2
+
+EXPORTED = ("bsp_attn_fwd", "bsp_skip_bitmap_words", "bsp_status_string", "bsp_last_error_detail",
+            "bsp_version")
+
+
+class BspError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"bsp_attn_fwd failed: {status_string(status)} ({detail})")
+        self.status = status
+        self.detail = detail
+
+
+class Tensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("stride_token", ctypes.c_int64),
+                ("stride_head", ctypes.c_int64), ("scale", ctypes.c_void_p)]
+
+
+class Seqs(ctypes.Structure):
+    _fields_ = [("cu_seqlens", ctypes.c_void_p), ("n_seqs", ctypes.c_int32), ("max_seqlen", ctypes.c_int32),
+                ("total_tokens", ctypes.c_int64)]
+
+
+class BlockTable(ctypes.Structure):
+    _fields_ = [("table", ctypes.c_void_p), ("max_pages_per_seq", ctypes.c_int32), ("page_size", ctypes.c_int32)]
+
+
+class SkipOut(ctypes.Structure):
+    _fields_ = [("bitmap", ctypes.c_void_p), ("bitmap_words", ctypes.c_int64), ("skip_count", ctypes.c_void_p),
+                ("visited_count", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python __graft_entry__.py` or "
+                           "`python block_sparse_long_bsp_amd/build.py`")
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    lib.bsp_attn_fwd.restype = ctypes.c_int
+    lib.bsp_attn_fwd.argtypes = [P, P, P, P, P, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                 ctypes.c_int, ctypes.c_float, P, P]
+    lib.bsp_skip_bitmap_words.restype = ctypes.c_int64
+    lib.bsp_skip_bitmap_words.argtypes = [ctypes.c_int] * 5
+    lib.bsp_status_string.restype = ctypes.c_char_p
+    lib.bsp_status_string.argtypes = [ctypes.c_int]
+    lib.bsp_last_error_detail.restype = ctypes.c_char_p
+    lib.bsp_last_error_detail.argtypes = []
+    lib.bsp_version.restype = ctypes.c_int
+    lib.bsp_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().bsp_status_string(int(status)).decode()
+
+
+def last_error_detail() -> str:
+    return load_library().bsp_last_error_detail().decode()
+
+
+def skip_bitmap_words(n_heads_q: int, n_seqs: int, max_seqlen: int, block_q: int, block_k: int) -> int:
+    return int(load_library().bsp_skip_bitmap_words(n_heads_q, n_seqs, max_seqlen, block_q, block_k))
+
+
+def fwd_raw(q: Tensor, k: Tensor, v: Tensor, o: Tensor, lse_ptr: int, seqs: Seqs, block_table: Optional[BlockTable],
+            n_heads_q: int, n_heads_kv: int, head_dim: int, block_q: int, block_k: int, lam: float,
+            skip_out: Optional[SkipOut], stream_ptr: int) -> int:
+    """Direct call of the C entry point with prepared descriptors; returns the status."""
+    lib = load_library()
+    bt = ctypes.byref(block_table) if block_table is not None else None
+    so = ctypes.byref(skip_out) if skip_out is not None else None
+    return int(lib.bsp_attn_fwd(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), ctypes.byref(o),
+                                ctypes.c_void_p(lse_ptr or None), ctypes.byref(seqs), bt, n_heads_q, n_heads_kv,
+                                head_dim, block_q, block_k, ctypes.c_float(lam), so,
+                                ctypes.c_void_p(stream_ptr or None)))
+
+
+_DT = {torch.float32: BSP_F32, torch.bfloat16: BSP_BF16}
+if hasattr(torch, "float8_e4m3fn"):
+    _DT[torch.float8_e4m3fn] = BSP_FP8_E4M3
+
+
+def _desc(x: torch.Tensor, scale: Optional[torch.Tensor] = None) -> Tensor:
+    if x.dim() != 3:
+        raise ValueError("expected a [tokens, heads, head_dim] tensor")
+    if x.stride(2) != 1:
+        raise ValueError("head_dim must be contiguous")
+    if x.dtype not in _DT:
+        raise ValueError(f"unsupported dtype {x.dtype}")
+    return Tensor(x.data_ptr(), _DT[x.dtype], x.stride(0), x.stride(1),
+                  scale.data_ptr() if scale is not None else None)
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor, max_seqlen: int, *,
+        block_table: Optional[torch.Tensor] = None, page_size: int = 64, block_q: int = 128, block_k: int = 128,
+        lam: float = math.inf, q_scale: Optional[torch.Tensor] = None, k_scale: Optional[torch.Tensor] = None,
+        v_scale: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+        lse: Optional[torch.Tensor] = None, bitmap: Optional[torch.Tensor] = None,
+        skip_count: Optional[torch.Tensor] = None, visited_count: Optional[torch.Tensor] = None,
+        want_bitmap: bool = True, want_lse: bool = True) -> Tuple[torch.Tensor, ...]:
+    """Block-sparse causal prefill attention on the current stream.
+
+    q [T, Hq, D]; k, v [T, Hkv, D] packed, or paged [n_pages, page_size, Hkv, D]
+    with ``block_table`` int32 [n_seqs, max_pages]. cu_seqlens int32 [n_seqs+1]
+    on the device. Returns (o, lse, bitmap, skip_count, visited_count); the
+    optional outputs are None when not requested. Output buffers may be passed
+    in to avoid allocation.
+    """
+    load_library()
+    if q.device.type != "cuda":
+        raise ValueError("q must be a device tensor")
+    T, Hq, D = q.shape
+    paged = block_table is not None
+    if paged:
+        if k.dim() != 4:
+            raise ValueError("paged k/v must be [n_pages, page_size, Hkv, D]")
+        page_size = k.shape[1]
+        k3 = k.view(k.shape[0] * k.shape[1], k.shape[2], k.shape[3])
+        v3 = v.view(v.shape[0] * v.shape[1], v.shape[2], v.shape[3])
+    else:
+        k3, v3 = k, v
+    Hkv = k3.shape[1]
+    n_seqs = cu_seqlens.numel() - 1
+    odt = torch.float32 if q.dtype == torch.float32 else torch.bfloat16
+    if out is None:
+        out = torch.empty((T, Hq, D), dtype=odt, device=q.device)
+    if want_lse and lse is None:
+        lse = torch.empty((Hq, T), dtype=torch.float32, device=q.device)
+    words = skip_bitmap_words(Hq, n_seqs, max_seqlen, block_q, block_k) if n_seqs > 0 else 0
+    if want_bitmap and bitmap is None:
+        bitmap = torch.empty((max(words, 1),), dtype=torch.int32, device=q.device)
+    if skip_count is None:
+        skip_count = torch.empty((Hq,), dtype=torch.int64, device=q.device)
+    if visited_count is None:
+        visited_count = torch.empty((Hq,), dtype=torch.int64, device=q.device)
+    seqs = Seqs(cu_seqlens.data_ptr(), n_seqs, int(max_seqlen), T)
+    bt = BlockTable(block_table.data_ptr(), block_table.shape[1], page_size) if paged else None
+    so = SkipOut(bitmap.data_ptr() if bitmap is not None else None, bitmap.numel() if bitmap is not None else 0,
+                 skip_count.data_ptr(), visited_count.data_ptr())
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = fwd_raw(_desc(q, q_scale), _desc(k3, k_scale), _desc(v3, v_scale), _desc(out), lse.data_ptr() if lse is not None else 0,
+                 seqs, bt, Hq, Hkv, D, block_q, block_k, float(lam), so, stream)
+    if st != BSP_OK:
+        raise BspError(st, last_error_detail())
+    return out, lse, bitmap, skip_count, visited_count
+
+
+def unpack_bitmap(bitmap: torch.Tensor, n_heads_q: int, n_seqs: int, max_seqlen: int, block_q: int,
+                  block_k: int):
+    """Host-side view of the bitmap as a bool numpy array [Hq, n_seqs, T_max, J_max]."""
+    import numpy as np
+
+    T = (max_seqlen + block_q - 1) // block_q
+    J = (max_seqlen + block_k - 1) // block_k
+    W = (J + 31) // 32
+    words = bitmap[: n_heads_q * n_seqs * T * W].cpu().numpy().view(np.uint32).reshape(n_heads_q, n_seqs, T, W)
+    bits = ((words[..., :, None] >> np.arange(32, dtype=np.uint32)) & 1).astype(bool)
+    return bits.reshape(n_heads_q, n_seqs, T, W * 32)[..., :J]

@@ -1,0 +1,749 @@
+// bsp_attn.hip -- causal block-sparse prefill attention with dynamic block
+// skipping inside the online softmax, for MI355X (gfx950, CDNA4).
+//
+// Method: page "长上下文推理加速方案部署实战：基于动态稀疏注意力机制的推理服务优化指南"
+// (deployment guide for a dynamic sparse attention kernel), section 3.2 and
+// section 6.1. For each (query tile, key block) pair the kernel computes the
+// block's scores, each row's local maximum, compares it with the running
+// maximum, and when every row's gap exceeds lambda it skips the
+// exponentials, the V-block load and the PV product.
+//
+// Kernel organisation (one workgroup = one query tile of one query head):
+//   * block_q/32 waves of 64 lanes; wave w owns 32 query rows.
+//   * scores are computed transposed, S^T = K Q^T, with 32x32 MFMA tiles:
+//     keys are the M dimension (read from LDS), queries the N dimension
+//     (held in registers for the whole tile). In the 32x32 accumulator
+//     layout lane l holds query (l % 32) and 16 keys, so every per-row
+//     reduction is 16 values in-lane plus one exchange with lane l ^ 32.
+//   * O^T = V^T P^T reuses the score accumulators directly as the B operand
+//     (bf16 path): the contraction index is permuted to match the
+//     accumulator layout and V is stored transposed in LDS with the same
+//     permutation.
+//   * the tile-wide skip decision is a wave vote (__all) followed by an
+//     LDS AND across the waves; V is loaded only for kept blocks.
+//   * work items are ordered heaviest tile first; when the KV head count is a
+//     multiple of 8 all query heads of one KV head run on one XCD (workgroup
+//     ids are dealt round-robin to the 8 XCDs), so its K/V stay in that
+//     XCD's L2.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "bsp_attn.h"
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+struct FwdParams {
+    const void *q;
+    const void *k;
+    const void *v;
+    void *o;
+    float *lse;
+    int64_t q_st, q_sh, k_st, k_sh, v_st, v_sh, o_st, o_sh;
+    int64_t lse_sh;                 // elements between heads of lse (= total tokens)
+    const int32_t *cu;              // cu_seqlens
+    const int32_t *table;           // paged: block table, else NULL
+    int32_t max_pages;
+    int32_t page_shift;             // log2(page_size)
+    uint32_t *bitmap;               // NULL: not written
+    unsigned long long *skip_count;
+    unsigned long long *visited_count;
+    int32_t n_seqs, T_max, W;       // W: bitmap words per (head, seq, tile) row
+    int32_t Hq, Hkv, G;
+    int32_t xcd_mode;               // 1: KV heads partitioned over the 8 XCDs
+    float c_log2;                   // softmax scale * log2(e)
+    float lam_raw;                  // lambda in raw dot-product units (lambda / scale)
+};
+
+constexpr float kLn2 = 0.69314718055994530942f;
+
+// Map the workgroup id to (sequence, query tile, query head). Tiles are dealt
+// from the last (heaviest under the causal mask) to the first.
+__device__ __forceinline__ void decode_item(const FwdParams &p, int &s, int &t, int &h) {
+    const int b = blockIdx.x;
+    if (p.xcd_mode) {
+        const int x = b & 7;
+        const int slot = b >> 3;
+        const int gpx = p.Hkv >> 3;                 // KV heads per XCD
+        const int per_tile = gpx * p.n_seqs * p.G;
+        const int tr = slot / per_tile;
+        int rem = slot - tr * per_tile;
+        const int gi = rem / (p.n_seqs * p.G);
+        rem -= gi * p.n_seqs * p.G;
+        s = rem / p.G;
+        const int e = rem - s * p.G;
+        h = (x + 8 * gi) * p.G + e;
+        t = p.T_max - 1 - tr;
+    } else {
+        const int per_tile = p.n_seqs * p.Hq;
+        const int tr = b / per_tile;
+        const int rem = b - tr * per_tile;
+        s = rem / p.Hq;
+        h = rem - s * p.Hq;
+        t = p.T_max - 1 - tr;
+    }
+}
+
+// Element offset of key/value row `kk` (sequence-local) of sequence s.
+template <bool PAGED>
+__device__ __forceinline__ int64_t kv_row(const FwdParams &p, int s, int base, int kk, int64_t st) {
+    if constexpr (PAGED) {
+        const int pg = p.table[(int64_t)s * p.max_pages + (kk >> p.page_shift)];
+        const int64_t slot = ((int64_t)pg << p.page_shift) + (kk & ((1 << p.page_shift) - 1));
+        return slot * st;
+    } else {
+        return (int64_t)(base + kk) * st;
+    }
+}
+
+__device__ __forceinline__ float wave_max16(const f32x16 &a) {
+    float m = fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3]));
+    m = fmaxf(m, fmaxf(fmaxf(a[4], a[5]), fmaxf(a[6], a[7])));
+    m = fmaxf(m, fmaxf(fmaxf(a[8], a[9]), fmaxf(a[10], a[11])));
+    m = fmaxf(m, fmaxf(fmaxf(a[12], a[13]), fmaxf(a[14], a[15])));
+    return m;
+}
+
+// Shared epilogue of the decision: record the bit and the count.
+struct SkipLog {
+    uint32_t word = 0;
+    int nskip = 0;
+};
+
+__device__ __forceinline__ void log_decision(const FwdParams &p, SkipLog &lg, int64_t row, int j, int nblk,
+                                             bool skip) {
+    if (skip) {
+        lg.word |= 1u << (j & 31);
+        ++lg.nskip;
+    }
+    if ((j & 31) == 31 || j == nblk - 1) {
+        if (p.bitmap != nullptr && threadIdx.x == 0) p.bitmap[row * p.W + (j >> 5)] = lg.word;
+        lg.word = 0;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 kernel: QK^T and PV on v_mfma_f32_32x32x16_bf16, fp32 accumulation.
+// ---------------------------------------------------------------------------
+template <int D, int BQ, int BK, bool PAGED>
+__global__ void __launch_bounds__(BQ * 2) fwd_bf16(FwdParams p) {
+    constexpr int NW = BQ / 32;
+    constexpr int NT = NW * 64;
+    constexpr int KS = D / 16;   // k-steps of S^T = K Q^T
+    constexpr int MT = BK / 32;  // 32-key tiles of a block
+    constexpr int DT = D / 32;   // 32-dim tiles of O^T
+    constexpr int PC = BK / 16;  // 16-key chunks of the PV contraction
+    constexpr int KSTR = D + 8;  // LDS row strides (elements), padded against bank conflicts
+    constexpr int VSTR = BK + 8;
+    __shared__ __attribute__((aligned(16))) __bf16 sK[BK * KSTR];
+    __shared__ __attribute__((aligned(16))) __bf16 sVt[D * VSTR];
+    __shared__ int sVote[NW];
+
+    int s, t, h;
+    decode_item(p, s, t, h);
+    const int base = p.cu[s];
+    const int L = p.cu[s + 1] - base;
+    if (t * BQ >= L) return;  // tile past the end of this sequence (bitmap row stays zero)
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = tid >> 6;
+    const int ln = lane & 31;  // query (N) / key or dim (M) index inside a 32-wide MFMA tile
+    const int hh = lane >> 5;  // lane half: selects the k sub-range of MFMA operands
+    const int g = h / p.G;
+    const int r1 = min((t + 1) * BQ, L);
+    const int nblk = (r1 - 1) / BK + 1;
+    const int q0 = t * BQ + w * 32;
+    const int qrow = q0 + ln;
+    const bool valid = qrow < L;
+    const int64_t bm_row = ((int64_t)h * p.n_seqs + s) * p.T_max + t;
+
+    const __bf16 *qg = (const __bf16 *)p.q;
+    const __bf16 *kg = (const __bf16 *)p.k;
+    const __bf16 *vg = (const __bf16 *)p.v;
+
+    // Q^T fragments (MFMA B operand): lane holds Q[qrow][16ks + 8hh .. +7].
+    bf16x8 qf[KS];
+    {
+        const __bf16 *qp = qg + (int64_t)(base + (valid ? qrow : 0)) * p.q_st + (int64_t)h * p.q_sh + 8 * hh;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            bf16x8 x = *(const bf16x8 *)(qp + 16 * ks);
+            if (!valid) x = bf16x8{};
+            qf[ks] = x;
+        }
+    }
+
+    float m_run = -INFINITY;  // running max of raw scores <q,k>
+    float l_run = 0.f;
+    f32x16 oacc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
+    SkipLog lg;
+
+    for (int j = 0; j < nblk; ++j) {
+        const int kb = j * BK;
+        __syncthreads();  // previous block's LDS reads are done
+        // ---- K block -> LDS, row-major [key][dim]
+#pragma unroll
+        for (int c = tid; c < BK * D / 8; c += NT) {
+            const int r = c / (D / 8);
+            const int c8 = c % (D / 8);
+            const int kk = kb + r;
+            bf16x8 x{};
+            if (kk < L) x = *(const bf16x8 *)(kg + kv_row<PAGED>(p, s, base, kk, p.k_st) + (int64_t)g * p.k_sh + 8 * c8);
+            *(bf16x8 *)&sK[r * KSTR + 8 * c8] = x;
+        }
+        __syncthreads();
+
+        // ---- S^T = K Q^T : sacc[mt] holds keys 32mt + 8(i/4) + 4hh + i%4 for query qrow
+        f32x16 sacc[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            f32x16 acc{};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 a = *(const bf16x8 *)&sK[(32 * mt + ln) * KSTR + 16 * ks + 8 * hh];
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], acc, 0, 0, 0);
+            }
+            sacc[mt] = acc;
+        }
+        // ---- causal mask (only where the block reaches past this wave's first query)
+        if (kb + BK - 1 > q0) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int key = kb + 32 * mt + 8 * (i >> 2) + 4 * hh + (i & 3);
+                    if (key > qrow) sacc[mt][i] = -INFINITY;
+                }
+        }
+        // ---- local max of each row over the block
+        float mloc = wave_max16(sacc[0]);
+#pragma unroll
+        for (int mt = 1; mt < MT; ++mt) mloc = fmaxf(mloc, wave_max16(sacc[mt]));
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+
+        // ---- skip decision: every valid row must have gap > lambda
+        const bool ok = !valid || (mloc == -INFINITY) || (m_run - mloc > p.lam_raw);
+        const int wall = __all(ok);
+        if (lane == 0) sVote[w] = wall;
+        __syncthreads();
+        bool skip = true;
+#pragma unroll
+        for (int x = 0; x < NW; ++x) skip = skip && (sVote[x] != 0);
+        log_decision(p, lg, bm_row, j, nblk, skip);
+        if (skip) continue;  // no exp, no V load, no PV
+
+        // ---- issue the V loads for this kept block (8x8 sub-blocks per thread)
+        constexpr int NSB = (BK / 8) * (D / 8);
+        constexpr int SBT = (NSB + NT - 1) / NT;
+        u32x4 vraw[SBT][8];
+#pragma unroll
+        for (int it = 0; it < SBT; ++it) {
+            const int sb = tid + it * NT;
+            const int kgl = sb & 7;
+            const int dgi = (sb >> 3) % (D / 8);
+            const int kgh = (sb >> 3) / (D / 8);
+            const int kgrp = kgh * 8 + kgl;
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                const int kk = kb + 8 * kgrp + r;
+                u32x4 x{};
+                if (sb < NSB && kk < L)
+                    x = *(const u32x4 *)(vg + kv_row<PAGED>(p, s, base, kk, p.v_st) + (int64_t)g * p.v_sh + 8 * dgi);
+                vraw[it][r] = x;
+            }
+        }
+
+        // ---- online softmax update (exp2 with the scale folded in)
+        const float m_new = fmaxf(m_run, mloc);
+        const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_run - m_new) * p.c_log2);
+        const float mc = m_new * p.c_log2;
+        float rs = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float e = __builtin_amdgcn_exp2f(fmaf(sacc[mt][i], p.c_log2, -mc));
+                sacc[mt][i] = e;
+                rs += e;
+            }
+        rs += __shfl_xor(rs, 32);
+        l_run = alpha * l_run + rs;
+        m_run = m_new;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+        bf16x8 pb[PC];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) pb[2 * mt + u][i] = (__bf16)sacc[mt][8 * u + i];
+
+        // ---- transpose the V sub-blocks into LDS as V^T [dim][key]
+#pragma unroll
+        for (int it = 0; it < SBT; ++it) {
+            const int sb = tid + it * NT;
+            if (sb < NSB) {
+                const int kgl = sb & 7;
+                const int dgi = (sb >> 3) % (D / 8);
+                const int kgh = (sb >> 3) / (D / 8);
+                const int kgrp = kgh * 8 + kgl;
+#pragma unroll
+                for (int dd = 0; dd < 8; ++dd) {
+                    u32x4 out;
+#pragma unroll
+                    for (int c2 = 0; c2 < 4; ++c2) {
+                        const uint32_t x = vraw[it][2 * c2][dd >> 1];
+                        const uint32_t y = vraw[it][2 * c2 + 1][dd >> 1];
+                        out[c2] = (dd & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
+                    }
+                    *(u32x4 *)&sVt[(8 * dgi + dd) * VSTR + 8 * kgrp] = out;
+                }
+            }
+        }
+        __syncthreads();
+
+        // ---- O^T += V^T P^T ; contraction chunk c covers keys 32mt + 16u + {0..3, 8..11} + 4hh
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const __bf16 *vr = &sVt[(32 * dt + ln) * VSTR];
+#pragma unroll
+            for (int c = 0; c < PC; ++c) {
+                const int k0 = 32 * (c >> 1) + 16 * (c & 1) + 4 * hh;
+                const bf16x4 lo = *(const bf16x4 *)(vr + k0);
+                const bf16x4 hi = *(const bf16x4 *)(vr + k0 + 8);
+                const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[c], oacc[dt], 0, 0, 0);
+            }
+        }
+    }
+
+    // ---- epilogue: normalise, store O (bf16) and LSE (natural log)
+    if (valid) {
+        const float inv = 1.f / l_run;
+        __bf16 *op = (__bf16 *)p.o + (int64_t)(base + qrow) * p.o_st + (int64_t)h * p.o_sh;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const bf16x4 x = {(__bf16)(oacc[dt][4 * g4 + 0] * inv), (__bf16)(oacc[dt][4 * g4 + 1] * inv),
+                                  (__bf16)(oacc[dt][4 * g4 + 2] * inv), (__bf16)(oacc[dt][4 * g4 + 3] * inv)};
+                *(bf16x4 *)(op + 32 * dt + 8 * g4 + 4 * hh) = x;
+            }
+        if (hh == 0 && p.lse != nullptr)
+            p.lse[(int64_t)h * p.lse_sh + base + qrow] = (m_run * p.c_log2 + __log2f(l_run)) * kLn2;
+    }
+    if (tid == 0) {
+        if (p.skip_count) atomicAdd(&p.skip_count[h], (unsigned long long)lg.nskip);
+        if (p.visited_count) atomicAdd(&p.visited_count[h], (unsigned long long)nblk);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 kernel: QK^T and PV on v_mfma_f32_32x32x2_f32 (one element per lane
+// per operand, so V needs no transpose).
+// ---------------------------------------------------------------------------
+template <int D, int BQ, int BK, bool PAGED>
+__global__ void __launch_bounds__(BQ * 2) fwd_f32(FwdParams p) {
+    constexpr int NW = BQ / 32;
+    constexpr int NT = NW * 64;
+    constexpr int KS = D / 2;
+    constexpr int MT = BK / 32;
+    constexpr int DT = D / 32;
+    constexpr int STR = D + 1;
+    __shared__ float sK[BK * STR];
+    __shared__ float sV[BK * STR];
+    __shared__ int sVote[NW];
+
+    int s, t, h;
+    decode_item(p, s, t, h);
+    const int base = p.cu[s];
+    const int L = p.cu[s + 1] - base;
+    if (t * BQ >= L) return;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = tid >> 6;
+    const int ln = lane & 31;
+    const int hh = lane >> 5;
+    const int g = h / p.G;
+    const int r1 = min((t + 1) * BQ, L);
+    const int nblk = (r1 - 1) / BK + 1;
+    const int q0 = t * BQ + w * 32;
+    const int qrow = q0 + ln;
+    const bool valid = qrow < L;
+    const int64_t bm_row = ((int64_t)h * p.n_seqs + s) * p.T_max + t;
+
+    const float *qg = (const float *)p.q;
+    const float *kg = (const float *)p.k;
+    const float *vg = (const float *)p.v;
+
+    float qf[KS];  // lane holds Q[qrow][2ks + hh]
+    {
+        const float *qp = qg + (int64_t)(base + (valid ? qrow : 0)) * p.q_st + (int64_t)h * p.q_sh + hh;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qf[ks] = valid ? qp[2 * ks] : 0.f;
+    }
+
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x16 oacc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
+    SkipLog lg;
+
+    for (int j = 0; j < nblk; ++j) {
+        const int kb = j * BK;
+        __syncthreads();
+        for (int c = tid; c < BK * D / 4; c += NT) {
+            const int r = c / (D / 4);
+            const int c4 = c % (D / 4);
+            const int kk = kb + r;
+            f32x4 x{};
+            if (kk < L) x = *(const f32x4 *)(kg + kv_row<PAGED>(p, s, base, kk, p.k_st) + (int64_t)g * p.k_sh + 4 * c4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sK[r * STR + 4 * c4 + e] = x[e];
+        }
+        __syncthreads();
+
+        f32x16 sacc[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            f32x16 acc{};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(sK[(32 * mt + ln) * STR + 2 * ks + hh], qf[ks], acc, 0, 0, 0);
+            sacc[mt] = acc;
+        }
+        if (kb + BK - 1 > q0) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int key = kb + 32 * mt + 8 * (i >> 2) + 4 * hh + (i & 3);
+                    if (key > qrow) sacc[mt][i] = -INFINITY;
+                }
+        }
+        float mloc = wave_max16(sacc[0]);
+#pragma unroll
+        for (int mt = 1; mt < MT; ++mt) mloc = fmaxf(mloc, wave_max16(sacc[mt]));
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+
+        const bool ok = !valid || (mloc == -INFINITY) || (m_run - mloc > p.lam_raw);
+        const int wall = __all(ok);
+        if (lane == 0) sVote[w] = wall;
+        __syncthreads();
+        bool skip = true;
+#pragma unroll
+        for (int x = 0; x < NW; ++x) skip = skip && (sVote[x] != 0);
+        log_decision(p, lg, bm_row, j, nblk, skip);
+        if (skip) continue;
+
+        for (int c = tid; c < BK * D / 4; c += NT) {
+            const int r = c / (D / 4);
+            const int c4 = c % (D / 4);
+            const int kk = kb + r;
+            f32x4 x{};
+            if (kk < L) x = *(const f32x4 *)(vg + kv_row<PAGED>(p, s, base, kk, p.v_st) + (int64_t)g * p.v_sh + 4 * c4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sV[r * STR + 4 * c4 + e] = x[e];
+        }
+
+        const float m_new = fmaxf(m_run, mloc);
+        const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_run - m_new) * p.c_log2);
+        const float mc = m_new * p.c_log2;
+        float rs = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float e = __builtin_amdgcn_exp2f(fmaf(sacc[mt][i], p.c_log2, -mc));
+                sacc[mt][i] = e;
+                rs += e;
+            }
+        rs += __shfl_xor(rs, 32);
+        l_run = alpha * l_run + rs;
+        m_run = m_new;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+        __syncthreads();
+
+        // O^T += V^T P^T: contraction step (mt, i) pairs key 32mt + 8(i/4) + 4hh + i%4 of both halves
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int key = 32 * mt + 8 * (i >> 2) + 4 * hh + (i & 3);
+                    oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(sV[key * STR + 32 * dt + ln], sacc[mt][i], oacc[dt],
+                                                                    0, 0, 0);
+                }
+    }
+
+    if (valid) {
+        const float inv = 1.f / l_run;
+        float *op = (float *)p.o + (int64_t)(base + qrow) * p.o_st + (int64_t)h * p.o_sh;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const f32x4 x = {oacc[dt][4 * g4 + 0] * inv, oacc[dt][4 * g4 + 1] * inv, oacc[dt][4 * g4 + 2] * inv,
+                                 oacc[dt][4 * g4 + 3] * inv};
+                *(f32x4 *)(op + 32 * dt + 8 * g4 + 4 * hh) = x;
+            }
+        if (hh == 0 && p.lse != nullptr)
+            p.lse[(int64_t)h * p.lse_sh + base + qrow] = (m_run * p.c_log2 + __log2f(l_run)) * kLn2;
+    }
+    if (tid == 0) {
+        if (p.skip_count) atomicAdd(&p.skip_count[h], (unsigned long long)lg.nskip);
+        if (p.visited_count) atomicAdd(&p.visited_count[h], (unsigned long long)nblk);
+    }
+}
+
+// Zero the bitmap and the counters ahead of the main kernel (a plain fill
+// kernel keeps the call free of memset nodes).
+__global__ void __launch_bounds__(256) fill_outputs(uint32_t *bitmap, int64_t words, unsigned long long *c0,
+                                                    unsigned long long *c1, int n_heads) {
+    const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    if (bitmap)
+        for (int64_t i = i0; i < words; i += stride) bitmap[i] = 0u;
+    if (i0 < n_heads) {
+        if (c0) c0[i0] = 0ull;
+        if (c1) c1[i0] = 0ull;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host side: validation, dispatch, launch.
+// ---------------------------------------------------------------------------
+thread_local char g_detail[512] = "";
+
+bsp_status_t fail(bsp_status_t st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+bsp_status_t fail(bsp_status_t st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_detail, sizeof(g_detail), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+int elem_size(int dtype) { return dtype == BSP_F32 ? 4 : dtype == BSP_BF16 ? 2 : dtype == BSP_FP8_E4M3 ? 1 : 0; }
+
+bool aligned16(const void *ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+bsp_status_t check_tensor(const char *name, const bsp_tensor_t *x, int heads, int head_dim) {
+    if (x == nullptr || x->data == nullptr) return fail(BSP_ERR_INVALID_ARG, "%s: NULL tensor or data", name);
+    const int es = elem_size(x->dtype);
+    if (es == 0) return fail(BSP_ERR_INVALID_ARG, "%s: unknown dtype %d", name, (int)x->dtype);
+    if (!aligned16(x->data)) return fail(BSP_ERR_INVALID_ARG, "%s: data pointer not 16-byte aligned", name);
+    const int64_t q = 16 / es;
+    if (x->stride_token <= 0 || x->stride_head <= 0 || x->stride_token % q != 0 || x->stride_head % q != 0)
+        return fail(BSP_ERR_INVALID_ARG, "%s: strides must be positive multiples of %lld elements", name, (long long)q);
+    if (heads > 1 && x->stride_head < head_dim)
+        return fail(BSP_ERR_INVALID_ARG, "%s: stride_head %lld < head_dim", name, (long long)x->stride_head);
+    return BSP_OK;
+}
+
+typedef void (*kernel_fn)(FwdParams);
+
+template <int D, int BQ, int BK>
+kernel_fn pick_kernel(int dtype, bool paged) {
+    if (dtype == BSP_BF16) return paged ? fwd_bf16<D, BQ, BK, true> : fwd_bf16<D, BQ, BK, false>;
+    if (dtype == BSP_F32) return paged ? fwd_f32<D, BQ, BK, true> : fwd_f32<D, BQ, BK, false>;
+    return nullptr;
+}
+
+kernel_fn find_kernel(int dtype, int D, int BQ, int BK, bool paged) {
+#define BSP_CASE(d, bq, bk) \
+    if (D == d && BQ == bq && BK == bk) return pick_kernel<d, bq, bk>(dtype, paged);
+    BSP_CASE(64, 64, 64)
+    BSP_CASE(64, 128, 64)
+    BSP_CASE(64, 128, 128)
+    BSP_CASE(128, 64, 64)
+    BSP_CASE(128, 128, 64)
+    BSP_CASE(128, 128, 128)
+#undef BSP_CASE
+    return nullptr;
+}
+
+std::mutex g_dev_mu;
+int g_dev_ok[64];  // 0 unknown, 1 gfx950, -1 other
+
+bsp_status_t check_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return fail(BSP_ERR_DEVICE, "no current HIP device");
+    }
+    if (dev >= 64) return fail(BSP_ERR_DEVICE, "device index %d out of range", dev);
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    if (g_dev_ok[dev] == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(BSP_ERR_DEVICE, "hipGetDeviceProperties failed for device %d", dev);
+        }
+        g_dev_ok[dev] = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+        if (g_dev_ok[dev] < 0) snprintf(g_detail, sizeof(g_detail), "device %d is %s, not gfx950", dev, prop.gcnArchName);
+    }
+    if (g_dev_ok[dev] < 0) return BSP_ERR_DEVICE;
+    return BSP_OK;
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+extern "C" {
+
+int bsp_version(void) { return 100; }
+
+const char *bsp_status_string(int status) {
+    switch (status) {
+        case BSP_OK: return "ok";
+        case BSP_ERR_INVALID_ARG: return "invalid argument";
+        case BSP_ERR_UNSUPPORTED: return "unsupported configuration";
+        case BSP_ERR_HIP: return "HIP error";
+        case BSP_ERR_DEVICE: return "device error";
+        default: return "unknown status";
+    }
+}
+
+const char *bsp_last_error_detail(void) { return g_detail; }
+
+int64_t bsp_skip_bitmap_words(int n_heads_q, int n_seqs, int max_seqlen, int block_q, int block_k) {
+    if (n_heads_q <= 0 || n_seqs < 0 || max_seqlen < 0 || block_q <= 0 || block_k <= 0) return 0;
+    const int64_t T = cdiv(max_seqlen, block_q);
+    const int64_t J = cdiv(max_seqlen, block_k);
+    const int64_t W = cdiv(J, 32);
+    return (int64_t)n_heads_q * n_seqs * T * W;
+}
+
+bsp_status_t bsp_attn_fwd(const bsp_tensor_t *q, const bsp_tensor_t *k, const bsp_tensor_t *v, bsp_tensor_t *o,
+                          float *lse, const bsp_seqs_t *seqs, const bsp_block_table_t *bt, int n_heads_q,
+                          int n_heads_kv, int head_dim, int block_q, int block_k, float lambda,
+                          bsp_skip_out_t *skip_out, void *stream) {
+    g_detail[0] = '\0';
+    // ---------------- argument checks (host only, before any HIP call)
+    if (n_heads_q <= 0 || n_heads_kv <= 0 || n_heads_q % n_heads_kv != 0)
+        return fail(BSP_ERR_INVALID_ARG, "n_heads_q (%d) must be a positive multiple of n_heads_kv (%d)", n_heads_q,
+                    n_heads_kv);
+    if (head_dim <= 0) return fail(BSP_ERR_INVALID_ARG, "head_dim must be positive");
+    if (isnan(lambda) || lambda < 0.f) return fail(BSP_ERR_INVALID_ARG, "lambda must be >= 0 or +inf (got %g)", lambda);
+    if (block_q <= 0 || block_k <= 0) return fail(BSP_ERR_INVALID_ARG, "block sizes must be positive");
+    bsp_status_t st;
+    if ((st = check_tensor("q", q, n_heads_q, head_dim)) != BSP_OK) return st;
+    if ((st = check_tensor("k", k, n_heads_kv, head_dim)) != BSP_OK) return st;
+    if ((st = check_tensor("v", v, n_heads_kv, head_dim)) != BSP_OK) return st;
+    if ((st = check_tensor("o", o, n_heads_q, head_dim)) != BSP_OK) return st;
+    if (k->dtype != q->dtype || v->dtype != q->dtype)
+        return fail(BSP_ERR_INVALID_ARG, "q, k and v must share one dtype");
+    const int want_o = q->dtype == BSP_F32 ? BSP_F32 : BSP_BF16;
+    if (o->dtype != want_o) return fail(BSP_ERR_INVALID_ARG, "o must be %s for this input dtype", want_o == BSP_F32 ? "f32" : "bf16");
+    if (q->dtype == BSP_FP8_E4M3 && (!q->scale || !k->scale || !v->scale))
+        return fail(BSP_ERR_INVALID_ARG, "fp8 inputs need per-head scales on q, k and v");
+    if (seqs == nullptr || seqs->cu_seqlens == nullptr) return fail(BSP_ERR_INVALID_ARG, "cu_seqlens is required");
+    if (seqs->n_seqs < 0 || seqs->max_seqlen < 0 || seqs->total_tokens < 0)
+        return fail(BSP_ERR_INVALID_ARG, "negative sequence sizes");
+    if (((uintptr_t)seqs->cu_seqlens & 3u) != 0) return fail(BSP_ERR_INVALID_ARG, "cu_seqlens not 4-byte aligned");
+    if (lse != nullptr && ((uintptr_t)lse & 3u) != 0) return fail(BSP_ERR_INVALID_ARG, "lse not 4-byte aligned");
+    const bool paged = bt != nullptr;
+    int page_shift = 0;
+    if (paged) {
+        if (bt->table == nullptr) return fail(BSP_ERR_INVALID_ARG, "block_table->table is NULL");
+        const int ps = bt->page_size;
+        if (ps <= 0 || (ps & (ps - 1)) != 0) return fail(BSP_ERR_INVALID_ARG, "page_size must be a power of two");
+        if (block_k % ps != 0 && ps % block_k != 0)
+            return fail(BSP_ERR_INVALID_ARG, "block_k (%d) and page_size (%d) must divide one another", block_k, ps);
+        while ((1 << page_shift) < ps) ++page_shift;
+        if ((int64_t)bt->max_pages_per_seq * ps < seqs->max_seqlen)
+            return fail(BSP_ERR_INVALID_ARG, "max_pages_per_seq * page_size < max_seqlen");
+    }
+    const int64_t T_max = cdiv(seqs->max_seqlen, block_q);
+    const int64_t J_max = cdiv(seqs->max_seqlen, block_k);
+    const int64_t W = cdiv(J_max, 32);
+    uint32_t *bitmap = skip_out ? skip_out->bitmap : nullptr;
+    const int64_t words = bsp_skip_bitmap_words(n_heads_q, seqs->n_seqs, seqs->max_seqlen, block_q, block_k);
+    if (bitmap != nullptr) {
+        if (((uintptr_t)bitmap & 3u) != 0) return fail(BSP_ERR_INVALID_ARG, "bitmap not 4-byte aligned");
+        if (skip_out->bitmap_words < words)
+            return fail(BSP_ERR_INVALID_ARG, "bitmap holds %lld words, %lld needed", (long long)skip_out->bitmap_words,
+                        (long long)words);
+    }
+    const int64_t grid64 = T_max * (int64_t)seqs->n_seqs * n_heads_q;
+    if (grid64 > 0x7fffffffLL) return fail(BSP_ERR_INVALID_ARG, "too many work items");
+    kernel_fn fn = find_kernel(q->dtype, head_dim, block_q, block_k, paged);
+    if (fn == nullptr)
+        return fail(BSP_ERR_UNSUPPORTED, "no kernel for dtype %d, head_dim %d, block_q %d, block_k %d", (int)q->dtype,
+                    head_dim, block_q, block_k);
+
+    // ---------------- device
+    if ((st = check_device()) != BSP_OK) return st;
+    hipStream_t hs = (hipStream_t)stream;
+    unsigned long long *c0 = skip_out ? skip_out->skip_count : nullptr;
+    unsigned long long *c1 = skip_out ? skip_out->visited_count : nullptr;
+    if (bitmap != nullptr || c0 != nullptr || c1 != nullptr) {
+        const int64_t work = words > n_heads_q ? words : n_heads_q;
+        const int blocks = (int)(cdiv(work, 256) < 1024 ? cdiv(work, 256) : 1024);
+        hipLaunchKernelGGL(fill_outputs, dim3(blocks > 0 ? blocks : 1), dim3(256), 0, hs, bitmap, words, c0, c1,
+                           n_heads_q);
+    }
+    if (grid64 > 0) {
+        FwdParams p;
+        memset(&p, 0, sizeof(p));
+        p.q = q->data;
+        p.k = k->data;
+        p.v = v->data;
+        p.o = o->data;
+        p.lse = lse;
+        p.q_st = q->stride_token;
+        p.q_sh = q->stride_head;
+        p.k_st = k->stride_token;
+        p.k_sh = k->stride_head;
+        p.v_st = v->stride_token;
+        p.v_sh = v->stride_head;
+        p.o_st = o->stride_token;
+        p.o_sh = o->stride_head;
+        p.lse_sh = seqs->total_tokens;
+        p.cu = seqs->cu_seqlens;
+        p.table = paged ? bt->table : nullptr;
+        p.max_pages = paged ? bt->max_pages_per_seq : 0;
+        p.page_shift = page_shift;
+        p.bitmap = bitmap;
+        p.skip_count = c0;
+        p.visited_count = c1;
+        p.n_seqs = seqs->n_seqs;
+        p.T_max = (int32_t)T_max;
+        p.W = (int32_t)W;
+        p.Hq = n_heads_q;
+        p.Hkv = n_heads_kv;
+        p.G = n_heads_q / n_heads_kv;
+        p.xcd_mode = (n_heads_kv % 8 == 0) ? 1 : 0;
+        const double scale = 1.0 / sqrt((double)head_dim);
+        p.c_log2 = (float)(scale * 1.4426950408889634);
+        p.lam_raw = isinf(lambda) ? INFINITY : (float)((double)lambda / scale);
+        hipLaunchKernelGGL(fn, dim3((unsigned)grid64), dim3(block_q * 2), 0, hs, p);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(BSP_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    return BSP_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,150 @@
+/*
+ * bsp_attn.h -- C ABI of the MI355X (gfx950) causal block-sparse prefill
+ * attention library, libbsp_attn.so.
+ *
+ * The operation is the dynamic sparse attention kernel of the page
+ * "长上下文推理加速方案部署实战：基于动态稀疏注意力机制的推理服务优化指南" (a deployment
+ * guide for a dynamic sparse attention kernel):
+ *   - section 3.2: inside the online softmax the kernel keeps the running
+ *     maximum of the scores; it takes key blocks in order, forms each block's
+ *     local maximum, and when the running maximum exceeds the local maximum by
+ *     more than lambda the block is negligible: its softmax exponentials, the
+ *     load of its V block and its product with V are all skipped. The decision
+ *     uses only intermediates the kernel already has.
+ *   - section 3.3 / 9.3: lambda is set at run time, per call.
+ *   - section 3.5: each call reports the skipped blocks (bitmap) and counts.
+ *   - section 5, step 3: the block size is a kernel parameter aligned with the
+ *     KV cache's page; section 5, step 4: paged KV cache and GQA.
+ *
+ * Semantics of one call (readings of what the page leaves open):
+ *   - causal attention per sequence, query i sees key j iff j <= i, with
+ *     score = <q, k> * s_q * s_k / sqrt(head_dim) (s_* = per-head fp8 scales,
+ *     1 for bf16/fp32).
+ *   - queries of a sequence are cut into tiles of block_q rows and keys into
+ *     blocks of block_k; tile t visits blocks 0 .. floor((last row)/block_k)
+ *     in ascending order. Block j is skipped for tile t of head h iff, for
+ *     EVERY valid row of the tile, (running max before block j) minus (the
+ *     row's max score inside block j) is strictly greater than lambda. Rows
+ *     with no visible key in the block never hold a skip back. Block 0 is never
+ *     skipped. lambda is in natural-log units of the scaled score; +inf gives
+ *     dense attention. Skipped keys leave numerator and denominator.
+ *   - o = sum_kept p v / sum_kept p (times s_v for fp8), lse = m + ln(l) over
+ *     the kept keys (natural log).
+ *
+ * Ownership: every pointer is caller-owned device memory (descriptors are
+ * host structs). The library allocates and frees nothing. A call only
+ * enqueues work on `stream` (a hipStream_t; NULL = the default stream) and
+ * returns without synchronising; results are valid once the stream reaches
+ * that point. Calls on different streams may run concurrently when their
+ * outputs do not overlap.
+ *
+ * Errors: return codes only; nothing throws across the ABI. All argument
+ * checks happen on the host before any HIP call, so a rejected call has no
+ * effect on the device. bsp_last_error_detail() describes the last non-OK
+ * status of the calling thread. Bad *device* data (cu_seqlens not
+ * non-decreasing, page ids out of range) is not checked and can fault.
+ */
+#ifndef BSP_ATTN_H
+#define BSP_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    BSP_OK = 0,
+    BSP_ERR_INVALID_ARG = 1,   /* NULL / misaligned pointer, inconsistent sizes, lambda NaN or < 0 */
+    BSP_ERR_UNSUPPORTED = 2,   /* (dtype, head_dim, block_q, block_k) without a compiled kernel */
+    BSP_ERR_HIP = 3,           /* a HIP launch error */
+    BSP_ERR_DEVICE = 4         /* no usable device, or the current device is not gfx950 */
+} bsp_status_t;
+
+typedef enum {
+    BSP_F32 = 0,
+    BSP_BF16 = 1,
+    BSP_FP8_E4M3 = 2           /* OCP e4m3 (max 448), per-head float scale */
+} bsp_dtype_t;
+
+/* A [tokens, heads, head_dim] tensor; head_dim is contiguous. Strides are in
+ * elements and the data pointer and both strides must give 16-byte aligned
+ * rows. For a paged K/V cache the "token" index is the slot index
+ * page * page_size + offset. */
+typedef struct {
+    void *data;                /* device pointer */
+    int32_t dtype;             /* bsp_dtype_t */
+    int64_t stride_token;      /* elements between consecutive tokens (slots) */
+    int64_t stride_head;       /* elements between consecutive heads */
+    const float *scale;        /* fp8 only: device float[heads] dequantisation scale; else NULL */
+} bsp_tensor_t;
+
+/* Packed variable-length batch (section 5 step 4: dynamic batching). */
+typedef struct {
+    const int32_t *cu_seqlens; /* device int32[n_seqs + 1]; cu[0] = 0, non-decreasing */
+    int32_t n_seqs;            /* host: number of sequences (>= 0) */
+    int32_t max_seqlen;        /* host: an upper bound of every sequence length */
+    int64_t total_tokens;      /* host: cu[n_seqs]; rows of q, o and the lse row length */
+} bsp_seqs_t;
+
+/* Paged K/V cache (section 5 step 4). NULL descriptor => K/V are packed like q. */
+typedef struct {
+    const int32_t *table;      /* device int32[n_seqs][max_pages_per_seq]: physical page of
+                                  logical page p of sequence s; only entries p < ceil(len/page) are read */
+    int32_t max_pages_per_seq;
+    int32_t page_size;         /* tokens per page: a power of two; block_k % page_size == 0
+                                  or page_size % block_k == 0 */
+} bsp_block_table_t;
+
+/* Per-call skip observability (section 3.5). */
+typedef struct {
+    uint32_t *bitmap;          /* device, may be NULL. Bit j of row ((h*n_seqs + s)*T_max + t),
+                                  where T_max = ceil(max_seqlen/block_q); each row is
+                                  W = ceil(ceil(max_seqlen/block_k)/32) uint32 words, LSB first.
+                                  1 = pair (tile t, block j) was visited and skipped. The whole
+                                  bitmap is rewritten by each call. */
+    int64_t bitmap_words;      /* capacity in words; >= bsp_skip_bitmap_words(...) when bitmap != NULL */
+    unsigned long long *skip_count;    /* device uint64[n_heads_q] or NULL: skipped pairs per head */
+    unsigned long long *visited_count; /* device uint64[n_heads_q] or NULL: visited pairs per head */
+} bsp_skip_out_t;
+
+/*
+ * bsp_attn_fwd -- causal block-sparse prefill attention forward.
+ *
+ * q   : [total_tokens, n_heads_q, head_dim]           dtype F32, BF16 or FP8_E4M3
+ * k, v: [total_tokens, n_heads_kv, head_dim] packed, or a paged cache
+ *       [n_pages * page_size, n_heads_kv, head_dim] when block_table != NULL;
+ *       same dtype as q.
+ * o   : [total_tokens, n_heads_q, head_dim]; F32 for F32 inputs, BF16 otherwise.
+ * lse : device float[n_heads_q][total_tokens] or NULL.
+ * cu_seqlens : sequence descriptor (required).
+ * block_table: paged-cache descriptor or NULL.
+ * n_heads_q % n_heads_kv == 0; query head h reads KV head h / (n_heads_q / n_heads_kv).
+ * head_dim in {64, 128}; (block_q, block_k) in {(64,64), (128,64), (128,128)}.
+ * lambda >= 0 or +inf (NaN and negative values are rejected).
+ * skip_mask_out: observability outputs or NULL.
+ * stream: hipStream_t (as void*), NULL for the default stream.
+ */
+bsp_status_t bsp_attn_fwd(const bsp_tensor_t *q, const bsp_tensor_t *k, const bsp_tensor_t *v,
+                          bsp_tensor_t *o, float *lse,
+                          const bsp_seqs_t *cu_seqlens, const bsp_block_table_t *block_table,
+                          int n_heads_q, int n_heads_kv, int head_dim, int block_q, int block_k,
+                          float lambda, bsp_skip_out_t *skip_mask_out, void *stream);
+
+/* Number of uint32 words the skip bitmap needs (0 for invalid arguments). */
+int64_t bsp_skip_bitmap_words(int n_heads_q, int n_seqs, int max_seqlen, int block_q, int block_k);
+
+/* Static text for a status code. */
+const char *bsp_status_string(int status);
+
+/* Thread-local description of the calling thread's last non-OK status. */
+const char *bsp_last_error_detail(void);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int bsp_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSP_ATTN_H */

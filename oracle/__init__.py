@@ -50,7 +50,7 @@ def load_library(path: str):
     lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
     lib.bsp_oracle_fwd.restype = ctypes.c_int
-    lib.bsp_oracle_fwd.argtypes = [P, P, P, P, P, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+    lib.bsp_oracle_fwd.argtypes = [P, P, P, ctypes.c_int, P, P, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                    ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double, P,
                                    ctypes.c_int64, P, ctypes.c_int, P, P, P, P, P, P, ctypes.c_int,
                                    ctypes.c_int]
@@ -94,6 +94,9 @@ class OracleResult:
     block_k: int
 
 
+_IN_DTYPES = {np.dtype(np.float32): 0, np.dtype(np.uint16): 1, np.dtype(np.uint8): 2}
+
+
 def run(q32: np.ndarray, k32: np.ndarray, v32: np.ndarray, cu_seqlens: np.ndarray,
         n_heads_q: int, n_heads_kv: int, block_q: int, block_k: int, lam: float,
         work: Optional[np.ndarray] = None, q_scale=None, k_scale=None, v_scale=None,
@@ -101,15 +104,19 @@ def run(q32: np.ndarray, k32: np.ndarray, v32: np.ndarray, cu_seqlens: np.ndarra
         j_max: Optional[int] = None) -> OracleResult:
     """Run the oracle on packed varlen inputs.
 
-    ``q32`` [T, Hq, D], ``k32``/``v32`` [T, Hkv, D] are the storage values
-    widened to float32; the optional per-head scales multiply them (fp8).
+    ``q32`` [T, Hq, D], ``k32``/``v32`` [T, Hkv, D] hold storage values: float32,
+    bf16 bit patterns (uint16) or fp8 e4m3 codes (uint8), all three of one
+    type; the optional per-head scales multiply them (fp8).
     ``work`` lists (seq, head, tile) triples; default: every tile of every head.
     ``forced`` [n, j_max] uint8 overrides decisions (0 keep, 1 skip, RULE).
     """
     lib = _load()
-    q32 = np.ascontiguousarray(q32, dtype=np.float32)
-    k32 = np.ascontiguousarray(k32, dtype=np.float32)
-    v32 = np.ascontiguousarray(v32, dtype=np.float32)
+    q32 = np.ascontiguousarray(q32)
+    k32 = np.ascontiguousarray(k32)
+    v32 = np.ascontiguousarray(v32)
+    if not (q32.dtype == k32.dtype == v32.dtype) or q32.dtype not in _IN_DTYPES:
+        raise ValueError("q, k, v must share one storage dtype (float32, uint16 bf16 bits, uint8 fp8 codes)")
+    in_dtype = _IN_DTYPES[q32.dtype]
     cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
     n_seqs = len(cu) - 1
     D = q32.shape[2]
@@ -138,7 +145,7 @@ def run(q32: np.ndarray, k32: np.ndarray, v32: np.ndarray, cu_seqlens: np.ndarra
     if forced is not None:
         forced = np.ascontiguousarray(forced, dtype=np.uint8)
         assert forced.shape == (n, j_max)
-    rc = lib.bsp_oracle_fwd(_ptr(q32), _ptr(k32), _ptr(v32), _ptr(sc[0]), _ptr(sc[1]), _ptr(sc[2]),
+    rc = lib.bsp_oracle_fwd(_ptr(q32), _ptr(k32), _ptr(v32), in_dtype, _ptr(sc[0]), _ptr(sc[1]), _ptr(sc[2]),
                             _ptr(cu), n_seqs, n_heads_q, n_heads_kv, D, block_q, block_k, float(lam),
                             _ptr(work), n, _ptr(forced), j_max, _ptr(o), _ptr(lse), _ptr(skip),
                             _ptr(visited), _ptr(mingap), _ptr(p), p_cols, int(n_threads))
@@ -150,7 +157,7 @@ def run(q32: np.ndarray, k32: np.ndarray, v32: np.ndarray, cu_seqlens: np.ndarra
 
 def run_inputs(inp, block_q: int, block_k: int, lam: float, **kw) -> OracleResult:
     """``run`` on a ``synth.Inputs`` object (fp8 scales applied)."""
-    return run(inp.q32, inp.k32, inp.v32, inp.cu_seqlens, inp.q.shape[1], inp.k.shape[1], block_q, block_k,
+    return run(inp.q, inp.k, inp.v, inp.cu_seqlens, inp.q.shape[1], inp.k.shape[1], block_q, block_k,
                lam, q_scale=inp.q_scale, k_scale=inp.k_scale, v_scale=inp.v_scale, **kw)
 
 

@@ -28,8 +28,9 @@
  *   - causal masking per sequence: key c is visible to query r iff c <= r.
  *   - LSE is m + ln(l) over the kept keys, natural log.
  *
- * Arithmetic: every input element is widened to double and multiplied by its
- * per-head dequantisation scale (1 when none is given); all sums, maxima,
+ * Arithmetic: every input element is widened exactly to double from its
+ * storage type (fp32; bf16 bit patterns; OCP fp8 e4m3 codes) and multiplied by
+ * its per-head dequantisation scale (1 when none is given); all sums, maxima,
  * exponentials and logarithms are in double precision.
  */
 #include <math.h>
@@ -43,13 +44,39 @@
 /* forced[] entries: 0 = keep, 1 = skip, anything else = apply the rule. */
 #define BSP_ORACLE_RULE 255
 
-int bsp_oracle_version(void) { return 1; }
+int bsp_oracle_version(void) { return 2; }
+
+/* Storage types of the inputs. */
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_FP8_E4M3 = 2 };
+
+/* Value of an OCP fp8 e4m3 code: s.eeee.mmm with exponent bias 7, exponent
+ * field 0 for subnormals (m/8 * 2^-6), 0x7F / 0xFF NaN, no infinities. */
+static double fp8_e4m3_value(uint8_t c)
+{
+    const int e = (c >> 3) & 15, m = c & 7;
+    if (e == 15 && m == 7) return NAN;
+    const double mag = (e == 0) ? ldexp(m / 8.0, -6) : ldexp(1.0 + m / 8.0, e - 7);
+    return (c & 0x80) ? -mag : mag;
+}
+
+/* Element i of a storage array, widened exactly to double. */
+static double elem(const void *base, size_t i, int dtype)
+{
+    if (dtype == ORACLE_F32) return (double)((const float *)base)[i];
+    if (dtype == ORACLE_BF16) {
+        const uint32_t u = (uint32_t)((const uint16_t *)base)[i] << 16;
+        float f;
+        memcpy(&f, &u, sizeof f);
+        return (double)f;
+    }
+    return fp8_e4m3_value(((const uint8_t *)base)[i]);
+}
 
 /*
  * bsp_oracle_fwd
  *
- * q  : float [total_tokens][n_heads_q][head_dim]   (storage values widened)
- * k,v: float [total_tokens][n_heads_kv][head_dim]
+ * q  : [total_tokens][n_heads_q][head_dim]   storage type `in_dtype`
+ * k,v: [total_tokens][n_heads_kv][head_dim]  same storage type
  * q_scale/k_scale/v_scale: double per head, or NULL (= 1.0)
  * cu_seqlens: int32 [n_seqs+1], cu[0] = 0, non-decreasing
  * work: int32 [n_work][3] = (sequence, query head, query tile)
@@ -66,7 +93,7 @@ int bsp_oracle_version(void) { return 1; }
  *             exactly 0 for masked and skipped keys.
  * Returns 0 on success, a negative number on invalid arguments.
  */
-int bsp_oracle_fwd(const float *q, const float *k, const float *v,
+int bsp_oracle_fwd(const void *q, const void *k, const void *v, int in_dtype,
                    const double *q_scale, const double *k_scale, const double *v_scale,
                    const int32_t *cu_seqlens, int n_seqs,
                    int n_heads_q, int n_heads_kv, int head_dim,
@@ -84,6 +111,8 @@ int bsp_oracle_fwd(const float *q, const float *k, const float *v,
         return -3;
     if (isnan(lambda) || lambda < 0.0)
         return -4;
+    if (in_dtype < ORACLE_F32 || in_dtype > ORACLE_FP8_E4M3)
+        return -6;
     const int group = n_heads_q / n_heads_kv;
     const double scale = 1.0 / sqrt((double)head_dim);
     const int D = head_dim;
@@ -149,7 +178,7 @@ int bsp_oracle_fwd(const float *q, const float *k, const float *v,
             for (int r = 0; r < nrows; ++r)
                 for (int d = 0; d < D; ++d)
                     qrow[(size_t)r * D + d] =
-                        (double)q[((size_t)(base + r0 + r) * n_heads_q + h) * D + d] * sq;
+                        elem(q, ((size_t)(base + r0 + r) * n_heads_q + h) * D + d, in_dtype) * sq;
 
             /* online-softmax state per query row */
             for (int r = 0; r < nrows; ++r) {
@@ -166,7 +195,7 @@ int bsp_oracle_fwd(const float *q, const float *k, const float *v,
                 for (int c = 0; c < nc; ++c)
                     for (int d = 0; d < D; ++d)
                         kblk[(size_t)c * D + d] =
-                            (double)k[((size_t)(base + c0 + c) * n_heads_kv + g) * D + d] * sk;
+                            elem(k, ((size_t)(base + c0 + c) * n_heads_kv + g) * D + d, in_dtype) * sk;
 
                 /* scaled scores with the causal mask, and the block's local max */
                 for (int r = 0; r < nrows; ++r) {
@@ -213,7 +242,7 @@ int bsp_oracle_fwd(const float *q, const float *k, const float *v,
                 for (int c = 0; c < nc; ++c)
                     for (int d = 0; d < D; ++d)
                         vblk[(size_t)c * D + d] =
-                            (double)v[((size_t)(base + c0 + c) * n_heads_kv + g) * D + d] * sv;
+                            elem(v, ((size_t)(base + c0 + c) * n_heads_kv + g) * D + d, in_dtype) * sv;
 
                 for (int r = 0; r < nrows; ++r) {
                     const double mnew = (mloc[r] > m[r]) ? mloc[r] : m[r];
@@ -253,7 +282,7 @@ int bsp_oracle_fwd(const float *q, const float *k, const float *v,
                             double dot = 0.0;
                             for (int d = 0; d < D; ++d)
                                 dot += qrow[(size_t)r * D + d] *
-                                       (double)k[((size_t)(base + c) * n_heads_kv + g) * D + d] * sk;
+                                       elem(k, ((size_t)(base + c) * n_heads_kv + g) * D + d, in_dtype) * sk;
                             p_w[(size_t)r * p_cols + c] = exp(scale * dot - m[r]) / l[r];
                         }
                     }

@@ -187,36 +187,52 @@ def _head_rng(code: int, seq: int, kv_head: int, salt: int = 0) -> np.random.Gen
     return np.random.Generator(np.random.PCG64(np.random.SeedSequence([BASE_SEED, code, _P_HEAD, seq, kv_head, salt])))
 
 
+def gen_group(L: int, G: int, D: int, rho: float, n_vert: int, code: int, seq: int, g: int, salt: int = 0,
+              sink_tokens: int = 4, sink_gain: float = 3.0, vert_gain: float = 2.0):
+    """Draw one KV head's group for one sequence: a list of G float32 query
+    arrays [L, D] and float32 k, v arrays [L, D]."""
+    rng = _head_rng(code, seq, g, salt)
+    c = math.sqrt(max(0.0, 1.0 - rho * rho))
+    e = rng.standard_normal((L, D))
+    if L > 1:
+        e[1:] *= c
+    x = lfilter([1.0], [1.0, -rho], e, axis=0) if L > 0 else e.copy()
+    np.multiply(x, 2.0, out=x)                 # x now holds 2 x_t
+    buf = e                                    # reuse the innovation buffer
+    qs = []
+    mu = np.zeros(D)
+    for _ in range(G):
+        rng.standard_normal(out=buf)
+        buf += x
+        if L > 0:
+            mu += buf.sum(axis=0)
+        qs.append(buf.astype(np.float32))
+    mu /= max(1, L * G)
+    rng.standard_normal(out=buf)
+    buf += x
+    k = buf
+    v = rng.standard_normal((L, D), dtype=np.float64).astype(np.float32)
+    ns = min(sink_tokens, L)
+    k[:ns] += sink_gain * mu
+    nv = min(n_vert, max(0, L - sink_tokens))
+    if nv > 0:
+        pos = rng.choice(np.arange(sink_tokens, L), size=nv, replace=False)
+        k[pos] += vert_gain * mu
+    return qs, k.astype(np.float32), v
+
+
 def gen_sequence(L: int, n_heads_q: int, n_heads_kv: int, D: int, rho: float, n_vert: int,
                  code: int, seq: int, salt: int = 0, sink_tokens: int = 4,
                  sink_gain: float = 3.0, vert_gain: float = 2.0):
-    """Draw float64 q [L, Hq, D], k/v [L, Hkv, D] for one sequence."""
+    """Draw float32 q [L, Hq, D], k/v [L, Hkv, D] for one sequence."""
     G = n_heads_q // n_heads_kv
-    q = np.empty((L, n_heads_q, D), dtype=np.float64)
-    k = np.empty((L, n_heads_kv, D), dtype=np.float64)
-    v = np.empty((L, n_heads_kv, D), dtype=np.float64)
-    c = math.sqrt(max(0.0, 1.0 - rho * rho))
+    qh, kh, vh = [], [], []
     for g in range(n_heads_kv):
-        rng = _head_rng(code, seq, g, salt)
-        e = rng.standard_normal((L, D))
-        if L > 1:
-            e[1:] *= c
-        x = lfilter([1.0], [1.0, -rho], e, axis=0) if L > 0 else e
-        mu = np.zeros(D)
-        for e_idx in range(G):
-            h = g * G + e_idx
-            q[:, h, :] = 2.0 * x + rng.standard_normal((L, D))
-            mu += q[:, h, :].sum(axis=0) if L > 0 else 0.0
-        mu /= max(1, L * G)
-        k[:, g, :] = 2.0 * x + rng.standard_normal((L, D))
-        v[:, g, :] = rng.standard_normal((L, D))
-        ns = min(sink_tokens, L)
-        k[:ns, g, :] += sink_gain * mu
-        nv = min(n_vert, max(0, L - sink_tokens))
-        if nv > 0:
-            pos = rng.choice(np.arange(sink_tokens, L), size=nv, replace=False)
-            k[pos, g, :] += vert_gain * mu
-    return q, k, v
+        qs, k, v = gen_group(L, G, D, rho, n_vert, code, seq, g, salt, sink_tokens, sink_gain, vert_gain)
+        qh += qs
+        kh.append(k)
+        vh.append(v)
+    return np.stack(qh, axis=1), np.stack(kh, axis=1), np.stack(vh, axis=1)
 
 
 @dataclass
@@ -224,13 +240,12 @@ class Inputs:
     """Host-side arrays for one (workload, dtype) case.
 
     ``q``/``k``/``v`` hold the storage values (float32, bf16 bits as uint16 or
-    fp8 codes as uint8) in packed varlen layout [total_tokens, heads, D].
-    ``q32``/``k32``/``v32`` are the same values widened exactly to float32 (fp8
-    codes decoded, *not* multiplied by their scale). ``q_scale``/``k_scale``/
-    ``v_scale`` are per-head float32 dequantisation scales (fp8 only, else None).
-    ``k_pages``/``v_pages`` hold the paged layout [n_pages, page_size, Hkv, D]
-    and ``block_table`` [n_seqs, max_pages] its page ids when the workload is
-    paged.
+    fp8 e4m3 codes as uint8) in packed varlen layout [total_tokens, heads, D].
+    ``q_scale``/``k_scale``/``v_scale`` are per-head float32 dequantisation
+    scales (fp8 only, else None). ``k_pages``/``v_pages`` hold the paged layout
+    [n_pages, page_size, Hkv, D] and ``block_table`` [n_seqs, max_pages] its
+    page ids when the workload is paged. ``q32``/``k32``/``v32`` widen the
+    storage values to float32 exactly (fp8 codes decoded, not scaled).
     """
     workload: Workload
     dtype: str
@@ -239,9 +254,6 @@ class Inputs:
     q: np.ndarray
     k: np.ndarray
     v: np.ndarray
-    q32: np.ndarray
-    k32: np.ndarray
-    v32: np.ndarray
     q_scale: Optional[np.ndarray] = None
     k_scale: Optional[np.ndarray] = None
     v_scale: Optional[np.ndarray] = None
@@ -258,58 +270,86 @@ class Inputs:
     def total_tokens(self) -> int:
         return int(self.cu_seqlens[-1])
 
+    def widen(self, a: np.ndarray) -> np.ndarray:
+        if self.dtype == "f32":
+            return a
+        if self.dtype == "bf16":
+            return bf16_to_f32(a)
+        return fp8_e4m3_to_f32(a)
 
-def _store(x64: np.ndarray, dtype: str, scale: Optional[np.ndarray]):
-    """Round float64 [T, H, D] values to storage; return (store, widened f32)."""
+    @property
+    def q32(self):
+        return self.widen(self.q)
+
+    @property
+    def k32(self):
+        return self.widen(self.k)
+
+    @property
+    def v32(self):
+        return self.widen(self.v)
+
+
+def _round_store(x32: np.ndarray, dtype: str, scale: Optional[float] = None) -> np.ndarray:
+    """Round float32 values to their storage type."""
     if dtype == "f32":
-        s = x64.astype(np.float32)
-        return s, s
+        return x32
     if dtype == "bf16":
-        s = bf16_round(x64.astype(np.float32))
-        return s, bf16_to_f32(s)
+        return bf16_round(x32)
     if dtype == "fp8":
-        s = fp8_e4m3_quantize(x64 / scale.astype(np.float64)[None, :, None])
-        return s, fp8_e4m3_to_f32(s)
+        return fp8_e4m3_quantize(x32.astype(np.float64) / float(scale))
     raise ValueError(dtype)
 
 
-def _fp8_scales(x64: np.ndarray) -> np.ndarray:
-    amax = np.abs(x64).max(axis=(0, 2)) if x64.size else np.ones(x64.shape[1])
-    return np.maximum(amax / FP8_E4M3_MAX, np.finfo(np.float32).tiny).astype(np.float32)
+_STORE_DT = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8}
 
 
 def build_inputs(seqlens: Sequence[int], n_heads_q: int, n_heads_kv: int, head_dim: int, dtype: str,
                  rho: float = 0.99, n_vert: int = 0, code: int = 0, salt: int = 0,
                  paged: bool = False, page_size: int = 64, workload: Optional[Workload] = None,
                  sink_tokens: int = 4, sink_gain: float = 3.0, vert_gain: float = 2.0) -> Inputs:
-    """Generate packed varlen inputs for arbitrary shapes (tests use small ones)."""
+    """Generate packed varlen inputs (any shape; the named workloads call this)."""
     seqlens = tuple(int(x) for x in seqlens)
     cu = np.zeros(len(seqlens) + 1, dtype=np.int32)
     cu[1:] = np.cumsum(seqlens)
     T = int(cu[-1])
-    q64 = np.empty((T, n_heads_q, head_dim))
-    k64 = np.empty((T, n_heads_kv, head_dim))
-    v64 = np.empty((T, n_heads_kv, head_dim))
+    G = n_heads_q // n_heads_kv
+    D = head_dim
+    # per sequence, per head float32 arrays (kept only until they are rounded)
+    per_seq = []
     for s, L in enumerate(seqlens):
-        qs, ks, vs = gen_sequence(L, n_heads_q, n_heads_kv, head_dim, rho, n_vert, code, s, salt,
-                                  sink_tokens, sink_gain, vert_gain)
-        q64[cu[s]:cu[s + 1]] = qs
-        k64[cu[s]:cu[s + 1]] = ks
-        v64[cu[s]:cu[s + 1]] = vs
-    qsc = ksc = vsc = None
+        qh, kh, vh = [], [], []
+        for g in range(n_heads_kv):
+            qs, k, v = gen_group(L, G, D, rho, n_vert, code, s, g, salt, sink_tokens, sink_gain, vert_gain)
+            qh += qs
+            kh.append(k)
+            vh.append(v)
+        per_seq.append((qh, kh, vh))
+    scales = [None, None, None]
     if dtype == "fp8":
-        qsc, ksc, vsc = _fp8_scales(q64), _fp8_scales(k64), _fp8_scales(v64)
-    q, q32 = _store(q64, dtype, qsc)
-    del q64
-    k, k32 = _store(k64, dtype, ksc)
-    v, v32 = _store(v64, dtype, vsc)
+        for i, H in enumerate((n_heads_q, n_heads_kv, n_heads_kv)):
+            amax = np.zeros(H)
+            for parts in per_seq:
+                for h, a in enumerate(parts[i]):
+                    if a.size:
+                        amax[h] = max(amax[h], float(np.abs(a).max()))
+            scales[i] = np.maximum(amax / FP8_E4M3_MAX, np.finfo(np.float32).tiny).astype(np.float32)
+    out = []
+    for i, H in enumerate((n_heads_q, n_heads_kv, n_heads_kv)):
+        dst = np.empty((T, H, D), dtype=_STORE_DT[dtype])
+        for s, parts in enumerate(per_seq):
+            heads = [_round_store(a, dtype, None if scales[i] is None else scales[i][h])
+                     for h, a in enumerate(parts[i])]
+            dst[cu[s]:cu[s + 1]] = np.stack(heads, axis=1) if heads and seqlens[s] > 0 else 0
+            parts[i].clear()
+        out.append(dst)
     w = workload
     if w is None:
         w = Workload(name="custom", seqlens=seqlens, n_heads_q=n_heads_q, n_heads_kv=n_heads_kv,
                      head_dim=head_dim, dtypes=(dtype,), block_q=0, block_k=0, lambdas=(), rho=rho,
                      n_vert=n_vert, paged=paged, page_size=page_size, code=code)
-    inp = Inputs(workload=w, dtype=dtype, seqlens=seqlens, cu_seqlens=cu, q=q, k=k, v=v,
-                 q32=q32, k32=k32, v32=v32, q_scale=qsc, k_scale=ksc, v_scale=vsc)
+    inp = Inputs(workload=w, dtype=dtype, seqlens=seqlens, cu_seqlens=cu, q=out[0], k=out[1], v=out[2],
+                 q_scale=scales[0], k_scale=scales[1], v_scale=scales[2])
     if paged:
         page_tensors(inp, page_size, code)
     return inp
@@ -329,19 +369,20 @@ def page_tensors(inp: Inputs, page_size: int, code: int = 0) -> None:
     perm = rng.permutation(P).astype(np.int32)
     table = np.zeros((len(inp.seqlens), max(1, maxp)), dtype=np.int32)
     Hkv, D = inp.k.shape[1], inp.k.shape[2]
-    kp = np.zeros((max(1, P), page_size, Hkv, D), dtype=inp.k.dtype)
-    vp = np.zeros((max(1, P), page_size, Hkv, D), dtype=inp.v.dtype)
+    slots = np.empty(inp.total_tokens, dtype=np.int64)   # physical slot of every packed token
     off = 0
     for s, L in enumerate(inp.seqlens):
-        base = int(inp.cu_seqlens[s])
-        for p in range(n_pages_seq[s]):
-            phys = int(perm[off + p])
-            table[s, p] = phys
-            lo = p * page_size
-            hi = min(L, lo + page_size)
-            kp[phys, : hi - lo] = inp.k[base + lo: base + hi]
-            vp[phys, : hi - lo] = inp.v[base + lo: base + hi]
+        table[s, : n_pages_seq[s]] = perm[off: off + n_pages_seq[s]]
+        tok = np.arange(L)
+        slots[inp.cu_seqlens[s]: inp.cu_seqlens[s + 1]] = table[s, tok // page_size].astype(np.int64) * page_size \
+            + tok % page_size
         off += n_pages_seq[s]
+    kp = np.zeros((max(1, P) * page_size, Hkv, D), dtype=inp.k.dtype)
+    vp = np.zeros((max(1, P) * page_size, Hkv, D), dtype=inp.v.dtype)
+    kp[slots] = inp.k
+    vp[slots] = inp.v
+    kp = kp.reshape(max(1, P), page_size, Hkv, D)
+    vp = vp.reshape(max(1, P), page_size, Hkv, D)
     inp.k_pages, inp.v_pages, inp.block_table, inp.page_size = kp, vp, table, page_size
 
 

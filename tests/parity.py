@@ -1,0 +1,177 @@
+"""Parity protocol between the HIP path and the CPU oracle (test infrastructure).
+
+For one (inputs, block sizes, lambda) case:
+  1. run the HIP library through its C ABI (``block_sparse_long_bsp_amd.fwd``);
+  2. run the oracle on the same inputs for a set of work items (all, or a
+     deterministic sample for large workloads);
+  3. the skip bitmaps must be identical on every visited pair whose decision
+     margin |min gap - lambda| exceeds 1e-3 (scores are fp32 on the GPU and
+     fp64 in the oracle, so pairs inside that band may legitimately flip);
+  4. where they differ inside the band, the oracle is re-run with the GPU's
+     decisions forced, and outputs are compared against that run;
+  5. O must satisfy the dtype's tolerance (bf16: max-abs <= 2e-2 and
+     mean-abs <= 2e-3; fp32: max-abs <= 1e-4; fp8: max-abs <= 6e-2) and LSE
+     |delta| <= 1e-2 (1e-4 for fp32);
+  6. per-head skip counts equal the bitmap's popcount and the visited counts
+     equal the causal pair count.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+
+import oracle
+import synth
+
+MARGIN_BAND = 1e-3
+TOL = {
+    "f32": dict(max_abs=1e-4, mean_abs=1e-4, lse=1e-4),
+    "bf16": dict(max_abs=2e-2, mean_abs=2e-3, lse=1e-2),
+    "fp8": dict(max_abs=6e-2, mean_abs=6e-3, lse=1e-2),
+}
+
+
+def to_device(inp: synth.Inputs, device="cuda"):
+    """Upload storage arrays as torch tensors; returns a dict of tensors."""
+    import torch
+
+    def conv(a, dtype):
+        if dtype == "f32":
+            return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+        if dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+        if dtype == "fp8":
+            return torch.from_numpy(np.ascontiguousarray(a)).to(device).view(torch.float8_e4m3fn)
+        raise ValueError(dtype)
+
+    d = dict(q=conv(inp.q, inp.dtype), k=conv(inp.k, inp.dtype), v=conv(inp.v, inp.dtype),
+             cu=torch.from_numpy(inp.cu_seqlens.astype(np.int32)).to(device))
+    if inp.k_pages is not None:
+        d["k_pages"] = conv(inp.k_pages, inp.dtype)
+        d["v_pages"] = conv(inp.v_pages, inp.dtype)
+        d["table"] = torch.from_numpy(inp.block_table.astype(np.int32)).to(device)
+    for nm in ("q_scale", "k_scale", "v_scale"):
+        a = getattr(inp, nm)
+        d[nm] = None if a is None else torch.from_numpy(a.astype(np.float32)).to(device)
+    return d
+
+
+def run_gpu(inp: synth.Inputs, dev: Dict, block_q: int, block_k: int, lam: float, paged: bool = False):
+    import torch
+
+    import block_sparse_long_bsp_amd as bsp
+
+    k = dev["k_pages"] if paged else dev["k"]
+    v = dev["v_pages"] if paged else dev["v"]
+    out = bsp.fwd(dev["q"], k, v, dev["cu"], inp.max_seqlen, block_table=dev.get("table") if paged else None,
+                  block_q=block_q, block_k=block_k, lam=lam, q_scale=dev["q_scale"], k_scale=dev["k_scale"],
+                  v_scale=dev["v_scale"])
+    torch.cuda.synchronize()
+    o, lse, bitmap, sc, vc = out
+    return dict(o=o.float().cpu().numpy(), lse=lse.cpu().numpy(),
+                bits=bsp.unpack_bitmap(bitmap, inp.q.shape[1], len(inp.seqlens), inp.max_seqlen, block_q, block_k),
+                skip_count=sc.cpu().numpy(), visited_count=vc.cpu().numpy())
+
+
+@dataclass
+class Report:
+    n_items: int = 0
+    n_pairs: int = 0
+    n_skipped: int = 0
+    n_band_flips: int = 0
+    max_abs: float = 0.0
+    mean_abs: float = 0.0
+    lse_max: float = 0.0
+    problems: List[str] = field(default_factory=list)
+
+    def ok(self):
+        return not self.problems
+
+
+def compare(inp: synth.Inputs, gpu: Dict, block_q: int, block_k: int, lam: float,
+            work: Optional[np.ndarray] = None, n_threads: int = 0, check_counts: bool = True) -> Report:
+    """Steps 2-6 of the protocol for the given work items (default: all)."""
+    Hq = inp.q.shape[1]
+    n_seqs = len(inp.seqlens)
+    J = max(1, (inp.max_seqlen + block_k - 1) // block_k)
+    ref = oracle.run_inputs(inp, block_q, block_k, lam, work=work, n_threads=n_threads, j_max=J)
+    rep = Report(n_items=ref.work.shape[0])
+    gbits = np.zeros_like(ref.skip)
+    for w, (s, h, t) in enumerate(ref.work):
+        gbits[w] = gpu["bits"][h, s, t, :J]
+    vis = ref.visited.astype(bool)
+    rep.n_pairs = int(vis.sum())
+    # bits outside the visited range must be zero
+    if np.any(gbits.astype(bool) & ~vis):
+        rep.problems.append("GPU bitmap has bits on unvisited pairs")
+    diff = (gbits != ref.skip) & vis
+    if diff.any():
+        margin = np.abs(ref.mingap - lam)
+        hard = diff & ~(margin <= MARGIN_BAND)
+        if hard.any():
+            idx = np.argwhere(hard)[:5]
+            rep.problems.append(f"{int(hard.sum())} skip decisions differ outside the margin band, e.g. "
+                                + ", ".join(f"item{tuple(ref.work[i])} block {j} gap {ref.mingap[i, j]:.6g}"
+                                            for i, j in idx))
+        rep.n_band_flips = int(diff.sum())
+        forced = np.where(vis, gbits, 0).astype(np.uint8)
+        ref = oracle.run_inputs(inp, block_q, block_k, lam, work=ref.work, forced=forced, n_threads=n_threads,
+                                j_max=J)
+    rep.n_skipped = int((ref.skip.astype(bool) & vis).sum())
+    cu = inp.cu_seqlens
+    tol = TOL[inp.dtype]
+    errs = []
+    lse_err = 0.0
+    for w, (s, h, t) in enumerate(ref.work):
+        L = int(cu[s + 1] - cu[s])
+        r0, r1 = t * block_q, min(L, (t + 1) * block_q)
+        if r1 <= r0:
+            continue
+        a, b = int(cu[s]) + r0, int(cu[s]) + r1
+        e = np.abs(gpu["o"][a:b, h, :].astype(np.float64) - ref.o[w, : r1 - r0])
+        errs.append(e.ravel())
+        le = np.abs(gpu["lse"][h, a:b].astype(np.float64) - ref.lse[w, : r1 - r0])
+        lse_err = max(lse_err, float(np.nanmax(le)) if le.size else 0.0)
+        if not np.all(np.isfinite(gpu["o"][a:b, h, :])):
+            rep.problems.append(f"non-finite output in item {(s, h, t)}")
+    if errs:
+        allerr = np.concatenate(errs)
+        rep.max_abs = float(allerr.max())
+        rep.mean_abs = float(allerr.mean())
+    rep.lse_max = lse_err
+    if rep.max_abs > tol["max_abs"]:
+        rep.problems.append(f"max-abs {rep.max_abs:.3g} > {tol['max_abs']}")
+    if rep.mean_abs > tol["mean_abs"]:
+        rep.problems.append(f"mean-abs {rep.mean_abs:.3g} > {tol['mean_abs']}")
+    if rep.lse_max > tol["lse"]:
+        rep.problems.append(f"LSE max error {rep.lse_max:.3g} > {tol['lse']}")
+    if check_counts:
+        bits = gpu["bits"]
+        pop = bits.reshape(Hq, -1).sum(axis=1)
+        if not np.array_equal(pop, gpu["skip_count"].astype(np.int64)):
+            rep.problems.append(f"skip_count {gpu['skip_count'][:4]}... != bitmap popcount {pop[:4]}...")
+        vis_expect = np.zeros(Hq, dtype=np.int64)
+        for s, L in enumerate(inp.seqlens):
+            for t in range((L + block_q - 1) // block_q):
+                r1 = min(L, (t + 1) * block_q)
+                vis_expect += (r1 - 1) // block_k + 1
+        if not np.array_equal(vis_expect, gpu["visited_count"].astype(np.int64)):
+            rep.problems.append(f"visited_count {gpu['visited_count'][:4]} != {vis_expect[:4]}")
+    return rep
+
+
+def check_case(inp: synth.Inputs, block_q: int, block_k: int, lams: Sequence[float], paged: bool = False,
+               work: Optional[np.ndarray] = None, dev=None) -> List[Report]:
+    """Run the GPU for each lambda and compare; raise AssertionError on any problem."""
+    dev = dev or to_device(inp)
+    reps = []
+    for lam in lams:
+        gpu = run_gpu(inp, dev, block_q, block_k, lam, paged=paged)
+        rep = compare(inp, gpu, block_q, block_k, lam, work=work)
+        reps.append(rep)
+        assert rep.ok(), f"lambda={lam}: " + "; ".join(rep.problems)
+    return reps

@@ -1,0 +1,171 @@
+"""Host-only checks of the C ABI (no GPU needed).
+
+The library must load, export every function declared in include/bsp_attn.h,
+compute the bitmap size, and reject invalid arguments with the documented
+status before touching the device (validation runs before any HIP call, so
+fake device addresses are never dereferenced here).
+"""
+
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+import block_sparse_long_bsp_amd as bsp
+from block_sparse_long_bsp_amd import BlockTable, Seqs, SkipOut, Tensor
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bsp_attn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bsp.LIB_PATH):
+        from block_sparse_long_bsp_amd import build
+
+        build.build()
+    return bsp.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bsp_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    assert "bsp_attn_fwd" in names
+    assert set(names) == set(bsp.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", bsp.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (bsp_[a-z_]+)\b", out))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_header_compiles_as_c():
+    src = '#include "bsp_attn.h"\nint main(void){ return (int)sizeof(bsp_tensor_t) > 0 ? 0 : 1; }\n'
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(HEADER), "-x", "c", "-",
+                        "-o", os.devnull], input=src, text=True, capture_output=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_struct_layouts_match_the_header():
+    # offsets of the ctypes mirrors against the C compiler's view of the header
+    prog = r'''
+#include <stdio.h>
+#include <stddef.h>
+#include "bsp_attn.h"
+int main(void) {
+  printf("%zu %zu %zu %zu %zu %zu\n", sizeof(bsp_tensor_t), offsetof(bsp_tensor_t, dtype),
+         offsetof(bsp_tensor_t, stride_token), offsetof(bsp_tensor_t, stride_head), offsetof(bsp_tensor_t, scale), (size_t)0);
+  printf("%zu %zu %zu %zu %zu %zu\n", sizeof(bsp_seqs_t), offsetof(bsp_seqs_t, n_seqs), offsetof(bsp_seqs_t, max_seqlen),
+         offsetof(bsp_seqs_t, total_tokens), sizeof(bsp_block_table_t), offsetof(bsp_block_table_t, page_size));
+  printf("%zu %zu %zu %zu %zu %zu\n", sizeof(bsp_skip_out_t), offsetof(bsp_skip_out_t, bitmap_words),
+         offsetof(bsp_skip_out_t, skip_count), offsetof(bsp_skip_out_t, visited_count), (size_t)0, (size_t)0);
+  return 0;
+}
+'''
+    exe = os.path.join("/tmp", "bsp_layout_%d" % os.getpid())
+    r = subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), "-x", "c", "-", "-o", exe], input=prog,
+                       text=True, capture_output=True)
+    assert r.returncode == 0, r.stderr
+    vals = [list(map(int, ln.split())) for ln in subprocess.run([exe], capture_output=True, text=True).stdout.split("\n") if ln]
+    os.unlink(exe)
+    assert vals[0][:5] == [ctypes.sizeof(Tensor), Tensor.dtype.offset, Tensor.stride_token.offset,
+                           Tensor.stride_head.offset, Tensor.scale.offset]
+    assert vals[1] == [ctypes.sizeof(Seqs), Seqs.n_seqs.offset, Seqs.max_seqlen.offset, Seqs.total_tokens.offset,
+                       ctypes.sizeof(BlockTable), BlockTable.page_size.offset]
+    assert vals[2][:4] == [ctypes.sizeof(SkipOut), SkipOut.bitmap_words.offset, SkipOut.skip_count.offset,
+                           SkipOut.visited_count.offset]
+
+
+def test_bitmap_words_formula(lib):
+    # rows of ceil(ceil(L/bk)/32) words per (head, seq, tile)
+    assert bsp.skip_bitmap_words(32, 1, 32768, 128, 128) == 32 * 256 * 8
+    assert bsp.skip_bitmap_words(32, 1, 131072, 128, 128) == 32 * 1024 * 32
+    assert bsp.skip_bitmap_words(1, 1, 1024, 64, 64) == 16
+    assert bsp.skip_bitmap_words(4, 3, 100, 64, 64) == 4 * 3 * 2 * 1
+    assert bsp.skip_bitmap_words(0, 1, 10, 64, 64) == 0
+    assert bsp.skip_bitmap_words(1, 1, 0, 64, 64) == 0
+
+
+def test_status_strings(lib):
+    assert bsp.status_string(0) == "ok"
+    assert "invalid" in bsp.status_string(1)
+    assert "unsupported" in bsp.status_string(2)
+    assert bsp.status_string(99) == "unknown status"
+    assert lib.bsp_version() >= 100
+
+
+FAKE = 0x10000  # 16-byte aligned address that is never dereferenced here
+
+
+def _call(**over):
+    """A valid-looking bf16 call with fake device addresses, with overrides."""
+    D = over.pop("head_dim", 128)
+    Hq = over.pop("n_heads_q", 32)
+    Hkv = over.pop("n_heads_kv", 8)
+    q = over.pop("q", Tensor(FAKE, bsp.BSP_BF16, Hq * D, D, None))
+    k = over.pop("k", Tensor(FAKE, bsp.BSP_BF16, Hkv * D, D, None))
+    v = over.pop("v", Tensor(FAKE, bsp.BSP_BF16, Hkv * D, D, None))
+    o = over.pop("o", Tensor(FAKE, bsp.BSP_BF16, Hq * D, D, None))
+    seqs = over.pop("seqs", Seqs(FAKE, 1, 256, 256))
+    bt = over.pop("bt", None)
+    bq = over.pop("block_q", 128)
+    bk = over.pop("block_k", 128)
+    lam = over.pop("lam", 4.0)
+    so = over.pop("so", SkipOut(FAKE, bsp.skip_bitmap_words(Hq, 1, 256, bq, bk), FAKE, FAKE))
+    assert not over
+    return bsp.fwd_raw(q, k, v, o, FAKE, seqs, bt, Hq, Hkv, D, bq, bk, lam, so, 0)
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(lam=float("nan")), bsp.BSP_ERR_INVALID_ARG),
+    (dict(lam=-0.5), bsp.BSP_ERR_INVALID_ARG),
+    (dict(n_heads_q=30), bsp.BSP_ERR_INVALID_ARG),
+    (dict(n_heads_kv=0), bsp.BSP_ERR_INVALID_ARG),
+    (dict(q=Tensor(0, bsp.BSP_BF16, 4096, 128, None)), bsp.BSP_ERR_INVALID_ARG),
+    (dict(q=Tensor(FAKE + 2, bsp.BSP_BF16, 4096, 128, None)), bsp.BSP_ERR_INVALID_ARG),
+    (dict(k=Tensor(FAKE, bsp.BSP_BF16, 1028, 128, None)), bsp.BSP_ERR_INVALID_ARG),
+    (dict(k=Tensor(FAKE, bsp.BSP_F32, 1024, 128, None)), bsp.BSP_ERR_INVALID_ARG),
+    (dict(o=Tensor(FAKE, bsp.BSP_F32, 4096, 128, None)), bsp.BSP_ERR_INVALID_ARG),
+    (dict(q=Tensor(FAKE, 7, 4096, 128, None)), bsp.BSP_ERR_INVALID_ARG),
+    (dict(seqs=Seqs(0, 1, 256, 256)), bsp.BSP_ERR_INVALID_ARG),
+    (dict(seqs=Seqs(FAKE, -1, 256, 256)), bsp.BSP_ERR_INVALID_ARG),
+    (dict(so=SkipOut(FAKE, 10, None, None)), bsp.BSP_ERR_INVALID_ARG),
+    (dict(bt=BlockTable(FAKE, 4, 48)), bsp.BSP_ERR_INVALID_ARG),       # not a power of two
+    (dict(bt=BlockTable(FAKE, 1, 64)), bsp.BSP_ERR_INVALID_ARG),       # too few pages for max_seqlen
+    (dict(bt=BlockTable(0, 4, 64)), bsp.BSP_ERR_INVALID_ARG),
+    (dict(head_dim=96, q=Tensor(FAKE, bsp.BSP_BF16, 32 * 96, 96, None), k=Tensor(FAKE, bsp.BSP_BF16, 8 * 96, 96, None),
+          v=Tensor(FAKE, bsp.BSP_BF16, 8 * 96, 96, None), o=Tensor(FAKE, bsp.BSP_BF16, 32 * 96, 96, None)),
+     bsp.BSP_ERR_UNSUPPORTED),
+    (dict(block_q=64, block_k=128), bsp.BSP_ERR_UNSUPPORTED),
+    (dict(block_q=32, block_k=32), bsp.BSP_ERR_UNSUPPORTED),
+])
+def test_invalid_arguments_rejected_before_the_device(lib, case, expect):
+    st = _call(**case)
+    assert st == expect, (st, bsp.last_error_detail())
+    assert bsp.last_error_detail() != ""
+
+
+def test_fp8_requires_scales(lib):
+    t = lambda: Tensor(FAKE, bsp.BSP_FP8_E4M3, 4096, 128, None)
+    kv = lambda: Tensor(FAKE, bsp.BSP_FP8_E4M3, 1024, 128, None)
+    st = _call(q=t(), k=kv(), v=kv())
+    assert st == bsp.BSP_ERR_INVALID_ARG
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    import importlib
+
+    r = subprocess.run(["python", "-c", "import block_sparse_long_bsp_amd as b; b.load_library('/nonexistent/lib.so')"],
+                       capture_output=True, text=True, cwd=ROOT)
+    assert r.returncode != 0 and "missing" in r.stderr

@@ -1,0 +1,209 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Small cases run the full oracle over several tiles with ragged tails, empty
+and single-token sequences, GQA, every compiled (head_dim, block_q, block_k)
+instance, packed and paged K/V. The named workloads run at their full sizes
+in the same launch configuration the benchmark uses, with the oracle on a
+deterministic sample of (sequence, head, tile) work items. The exact
+reductions (GQA == repeated-KV MHA, identity page table == packed, packed
+varlen == separate sequences, bitwise repeatability) compare GPU outputs
+bit for bit.
+"""
+
+import math
+import os
+
+import numpy as np
+import pytest
+
+import synth
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_sparse_long_bsp_amd as bsp
+
+    bsp.load_library()
+    yield
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+INSTANCES = [(64, 64, 64), (64, 128, 64), (64, 128, 128), (128, 64, 64), (128, 128, 64), (128, 128, 128)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("inst", INSTANCES, ids=lambda x: "d%d_q%d_k%d" % x)
+@pytest.mark.parametrize("paged", [False, True], ids=["packed", "paged"])
+def test_small_cases(dtype, inst, paged):
+    D, bq, bk = inst
+    seqlens = (300, 0, 129, 1, 64)
+    page = 64 if bk >= 64 else bk
+    # strong sink keys make many blocks skippable at small lambda for every tile shape
+    inp = synth.build_inputs(seqlens, 4, 2, D, dtype, rho=0.95, n_vert=2, code=201, paged=paged, page_size=page,
+                             sink_gain=6.0)
+    _log(f"small case dtype={dtype} D={D} bq={bq} bk={bk} paged={paged}")
+    reps = parity.check_case(inp, bq, bk, [math.inf, 2.0, 0.0], paged=paged)
+    assert reps[0].n_skipped == 0
+    assert reps[2].n_skipped > 0
+
+
+def test_xcd_mapping_with_eight_kv_heads():
+    # 8 KV heads switch on the XCD-partitioned work order
+    inp = synth.build_inputs((517, 130), 16, 8, 128, "bf16", rho=0.97, n_vert=4, code=202)
+    _log("xcd mapping case")
+    parity.check_case(inp, 128, 64, [math.inf, 3.0])
+
+
+def test_paged_small_pages():
+    inp = synth.build_inputs((200, 77), 4, 1, 128, "bf16", rho=0.97, code=203, paged=True, page_size=16)
+    _log("paged page_size=16")
+    parity.check_case(inp, 64, 64, [math.inf, 1.0], paged=True)
+
+
+def test_single_1k_fp32_full():
+    w = synth.WORKLOADS["single_1k_fp32"]
+    inp = synth.make_workload(w.name)
+    _log("single_1k_fp32")
+    reps = parity.check_case(inp, w.block_q, w.block_k, list(w.lambdas))
+    _log(f"  skipped {[r.n_skipped for r in reps]} of {reps[0].n_pairs}; max-abs {[r.max_abs for r in reps]}")
+
+
+def _sampled(name, heads, tile_stride, dtype=None):
+    w = synth.WORKLOADS[name]
+    inp = synth.make_workload(name, dtype)
+    work = synth.work_items(inp.seqlens, w.n_heads_q, w.block_q, heads=heads, tile_stride=tile_stride)
+    _log(f"{name} {inp.dtype}: {work.shape[0]} sampled work items")
+    reps = parity.check_case(inp, w.block_q, w.block_k, list(w.lambdas), paged=w.paged, work=work)
+    for lam, r in zip(w.lambdas, reps):
+        _log(f"  lambda={lam}: skipped {r.n_skipped}/{r.n_pairs} band flips {r.n_band_flips} "
+             f"max-abs {r.max_abs:.3g} mean-abs {r.mean_abs:.3g} lse {r.lse_max:.3g}")
+    return reps
+
+
+def test_llama8b_8k_bf16_sampled():
+    _sampled("llama8b_8k_bf16", heads=[0, 13, 31], tile_stride=7)
+
+
+def test_llama8b_32k_bf16_sampled():
+    _sampled("llama8b_32k_bf16", heads=[0, 21], tile_stride=51)
+
+
+def test_varlen16_paged_bf16_sampled():
+    _sampled("varlen16_paged_bf16", heads=[5, 30], tile_stride=37)
+
+
+def test_repeat_runs_are_bit_identical():
+    import torch
+
+    import block_sparse_long_bsp_amd as bsp
+
+    inp = synth.build_inputs((700, 45), 8, 2, 128, "bf16", rho=0.97, code=204)
+    dev = parity.to_device(inp)
+    outs = []
+    for _ in range(3):
+        o, lse, bm, sc, vc = bsp.fwd(dev["q"], dev["k"], dev["v"], dev["cu"], inp.max_seqlen, block_q=128,
+                                     block_k=64, lam=2.0)
+        torch.cuda.synchronize()
+        outs.append((o.clone(), lse.clone(), bm.clone(), sc.clone()))
+    for x in outs[1:]:
+        for a, b in zip(outs[0], x):
+            assert torch.equal(a, b)
+
+
+def test_gqa_equals_repeated_kv_mha():
+    import torch
+
+    import block_sparse_long_bsp_amd as bsp
+
+    inp = synth.build_inputs((333,), 8, 2, 128, "bf16", rho=0.97, code=205)
+    dev = parity.to_device(inp)
+    a = bsp.fwd(dev["q"], dev["k"], dev["v"], dev["cu"], inp.max_seqlen, block_q=128, block_k=128, lam=1.5)
+    k4 = dev["k"].repeat_interleave(4, dim=1).contiguous()
+    v4 = dev["v"].repeat_interleave(4, dim=1).contiguous()
+    b = bsp.fwd(dev["q"], k4, v4, dev["cu"], inp.max_seqlen, block_q=128, block_k=128, lam=1.5)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_identity_block_table_equals_packed():
+    import torch
+
+    import block_sparse_long_bsp_amd as bsp
+
+    L = 320
+    inp = synth.build_inputs((L,), 4, 2, 128, "bf16", rho=0.97, code=206)
+    dev = parity.to_device(inp)
+    kp = dev["k"].view(L // 64, 64, 2, 128)
+    vp = dev["v"].view(L // 64, 64, 2, 128)
+    table = torch.arange(L // 64, dtype=torch.int32, device="cuda").view(1, -1)
+    a = bsp.fwd(dev["q"], dev["k"], dev["v"], dev["cu"], L, block_q=64, block_k=64, lam=1.0)
+    b = bsp.fwd(dev["q"], kp, vp, dev["cu"], L, block_table=table, block_q=64, block_k=64, lam=1.0)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_packed_varlen_equals_separate_calls():
+    import torch
+
+    import block_sparse_long_bsp_amd as bsp
+
+    seqlens = (130, 0, 257, 64)
+    inp = synth.build_inputs(seqlens, 4, 2, 128, "bf16", rho=0.97, code=207)
+    dev = parity.to_device(inp)
+    o, lse, bm, sc, vc = bsp.fwd(dev["q"], dev["k"], dev["v"], dev["cu"], max(seqlens), block_q=128, block_k=64,
+                                 lam=2.0)
+    cu = inp.cu_seqlens
+    bits = bsp.unpack_bitmap(bm, 4, len(seqlens), max(seqlens), 128, 64)
+    for s, L in enumerate(seqlens):
+        if L == 0:
+            assert not bits[:, s].any()
+            continue
+        a, b = int(cu[s]), int(cu[s + 1])
+        one = torch.tensor([0, L], dtype=torch.int32, device="cuda")
+        o1, l1, b1, _, _ = bsp.fwd(dev["q"][a:b], dev["k"][a:b], dev["v"][a:b], one, L, block_q=128, block_k=64,
+                                   lam=2.0)
+        torch.cuda.synchronize()
+        assert torch.equal(o[a:b], o1)
+        assert torch.equal(lse[:, a:b], l1)
+        bits1 = bsp.unpack_bitmap(b1, 4, 1, L, 128, 64)
+        T1, J1 = bits1.shape[2], bits1.shape[3]
+        assert np.array_equal(bits[:, s, :T1, :J1], bits1[:, 0])
+
+
+def test_repeated_calls_allocate_nothing_in_the_library():
+    import torch
+
+    import block_sparse_long_bsp_amd as bsp
+
+    inp = synth.build_inputs((512,), 8, 2, 128, "bf16", rho=0.97, code=208)
+    dev = parity.to_device(inp)
+    o, lse, bm, sc, vc = bsp.fwd(dev["q"], dev["k"], dev["v"], dev["cu"], 512, block_q=128, block_k=128, lam=2.0)
+    torch.cuda.synchronize()
+    before = torch.cuda.mem_get_info()[0]
+    for _ in range(200):
+        bsp.fwd(dev["q"], dev["k"], dev["v"], dev["cu"], 512, block_q=128, block_k=128, lam=2.0, out=o, lse=lse,
+                bitmap=bm, skip_count=sc, visited_count=vc)
+    torch.cuda.synchronize()
+    after = torch.cuda.mem_get_info()[0]
+    assert before - after < (8 << 20)
+
+
+def test_single_hip_runtime_in_process():
+    import block_sparse_long_bsp_amd as bsp
+
+    bsp.load_library()
+    maps = open("/proc/self/maps").read()
+    paths = {ln.split()[-1] for ln in maps.splitlines() if "libamdhip64" in ln}
+    assert len(paths) == 1, paths

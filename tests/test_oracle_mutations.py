@@ -35,8 +35,11 @@ MUTANTS = {
     "masked_row_blocks": [("gap = INFINITY;             /* nothing visible in this block */",
                            "gap = -INFINITY;")],
     "k_scale_ignored": [("const double sk = k_scale ? k_scale[g] : 1.0;", "const double sk = 1.0;")],
-    "v_offset": [("(double)v[((size_t)(base + c0 + c) * n_heads_kv + g) * D + d] * sv;",
-                  "(double)v[((size_t)(base + c0 + (c + 1) % nc) * n_heads_kv + g) * D + d] * sv;")],
+    "v_offset": [("elem(v, ((size_t)(base + c0 + c) * n_heads_kv + g) * D + d, in_dtype) * sv;",
+                  "elem(v, ((size_t)(base + c0 + (c + 1) % nc) * n_heads_kv + g) * D + d, in_dtype) * sv;")],
+    "bf16_widen_shift": [("const uint32_t u = (uint32_t)((const uint16_t *)base)[i] << 16;",
+                          "const uint32_t u = (uint32_t)((const uint16_t *)base)[i] << 15;")],
+    "fp8_bias": [("ldexp(1.0 + m / 8.0, e - 7)", "ldexp(1.0 + m / 8.0, e - 8)")],
 }
 
 
@@ -54,7 +57,9 @@ def _pin_calls():
               pins.test_golden_worked_examples,
               pins.test_tie_at_lambda_is_kept_on_random_integer_scores,
               pins.test_fp8_scales_are_applied_per_head,
-              pins.test_gqa_equals_repeated_mha]
+              pins.test_gqa_equals_repeated_mha,
+              lambda: pins.test_storage_types_widen_exactly("bf16"),
+              lambda: pins.test_storage_types_widen_exactly("fp8")]
     return calls
 
 

@@ -400,6 +400,21 @@ def test_fp8_scales_are_applied_per_head():
     np.testing.assert_allclose(LSE, LSE_ref, rtol=1e-14, atol=1e-12)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_storage_types_widen_exactly(dtype):
+    # the oracle widens bf16 bit patterns / fp8 codes itself; the result must be
+    # bit-identical to a run on the same values widened by numpy to float32
+    inp = synth.build_inputs((70, 33), 4, 2, 16, dtype, rho=0.9, code=103)
+    a = oracle.run_inputs(inp, 16, 16, 1.0)
+    b = oracle.run(inp.q32, inp.k32, inp.v32, inp.cu_seqlens, 4, 2, 16, 16, 1.0,
+                   q_scale=inp.q_scale, k_scale=inp.k_scale, v_scale=inp.v_scale)
+    assert np.array_equal(a.o, b.o) and np.array_equal(a.skip, b.skip)
+    assert np.array_equal(a.lse, b.lse, equal_nan=True)
+    # and the widened values are the storage type's exact values
+    if dtype == "bf16":
+        assert np.array_equal(inp.q32.view(np.uint32) & 0xFFFF, np.zeros_like(inp.q32.view(np.uint32)))
+
+
 def test_deterministic_across_runs_and_thread_counts():
     inp = small_inputs((130, 60), 4, 2, 16, salt=12)
     a = oracle.run_inputs(inp, 32, 16, 1.0, n_threads=1)
