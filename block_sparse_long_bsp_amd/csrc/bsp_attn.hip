@@ -64,35 +64,40 @@ struct FwdParams {
     int32_t n_seqs, T_max, W;       // W: bitmap words per (head, seq, tile) row
     int32_t Hq, Hkv, G;
     int32_t xcd_mode;               // 1: KV heads partitioned over the 8 XCDs
+    int32_t hpw;                    // query heads per workgroup (divides G)
     float c_log2;                   // softmax scale * log2(e)
     float lam_raw;                  // lambda in raw dot-product units (lambda / scale)
 };
 
 constexpr float kLn2 = 0.69314718055994530942f;
 
-// Map the workgroup id to (sequence, query tile, query head). Tiles are dealt
-// from the last (heaviest under the causal mask) to the first.
-__device__ __forceinline__ void decode_item(const FwdParams &p, int &s, int &t, int &h) {
+// Map the workgroup id to (sequence, query tile, head group of HPW query heads
+// that share one KV head). Tiles are dealt from the last (heaviest under the
+// causal mask) to the first; in XCD mode the head groups of KV head x + 8i
+// all run on XCD x.
+__device__ __forceinline__ void decode_item(const FwdParams &p, int &s, int &t, int &hp) {
     const int b = blockIdx.x;
+    const int Gp = p.G / p.hpw;          // head groups per KV head
     if (p.xcd_mode) {
         const int x = b & 7;
         const int slot = b >> 3;
-        const int gpx = p.Hkv >> 3;                 // KV heads per XCD
-        const int per_tile = gpx * p.n_seqs * p.G;
+        const int gpx = p.Hkv >> 3;      // KV heads per XCD
+        const int per_tile = gpx * p.n_seqs * Gp;
         const int tr = slot / per_tile;
         int rem = slot - tr * per_tile;
-        const int gi = rem / (p.n_seqs * p.G);
-        rem -= gi * p.n_seqs * p.G;
-        s = rem / p.G;
-        const int e = rem - s * p.G;
-        h = (x + 8 * gi) * p.G + e;
+        const int gi = rem / (p.n_seqs * Gp);
+        rem -= gi * p.n_seqs * Gp;
+        s = rem / Gp;
+        const int e = rem - s * Gp;
+        hp = (x + 8 * gi) * Gp + e;
         t = p.T_max - 1 - tr;
     } else {
-        const int per_tile = p.n_seqs * p.Hq;
+        const int Hp = p.Hq / p.hpw;
+        const int per_tile = p.n_seqs * Hp;
         const int tr = b / per_tile;
         const int rem = b - tr * per_tile;
-        s = rem / p.Hq;
-        h = rem - s * p.Hq;
+        s = rem / Hp;
+        hp = rem - s * Hp;
         t = p.T_max - 1 - tr;
     }
 }
@@ -124,36 +129,78 @@ struct SkipLog {
 };
 
 __device__ __forceinline__ void log_decision(const FwdParams &p, SkipLog &lg, int64_t row, int j, int nblk,
-                                             bool skip) {
+                                             bool skip, bool writer) {
     if (skip) {
         lg.word |= 1u << (j & 31);
         ++lg.nskip;
     }
     if ((j & 31) == 31 || j == nblk - 1) {
-        if (p.bitmap != nullptr && threadIdx.x == 0) p.bitmap[row * p.W + (j >> 5)] = lg.word;
+        if (p.bitmap != nullptr && writer) p.bitmap[row * p.W + (j >> 5)] = lg.word;
         lg.word = 0;
     }
 }
 
 // ---------------------------------------------------------------------------
 // bf16 kernel: QK^T and PV on v_mfma_f32_32x32x16_bf16, fp32 accumulation.
+//
+// A workgroup serves one query tile of HPW query heads that share a KV head
+// (GQA grouping), with block_q/32 waves per head; K and V blocks are staged
+// once in LDS for all of them. K and V move from global memory straight into
+// LDS (global_load_lds, 16 bytes per lane), double-buffered, in row-major
+// [key][dim] order with the 16-byte chunks of each row XOR-swizzled so that
+// both the QK^T operand reads (ds_read_b128 along dim) and the transposing
+// PV operand reads (ds_read_b64_tr_b16, which hands each lane four keys of one
+// dim) are free of bank conflicts.
+//
+// Per key block j:
+//   1. start the copy of K_{j+1} into the other K buffer;
+//   2. S^T = K_j Q^T; causal mask on the diagonal block; row maxima; per-head
+//      vote; barrier B1;
+//   3. sparse mode: start the copy of V_j only if some head keeps block j;
+//      dense mode (lambda = +inf, nothing can be skipped): start the copy of
+//      V_{j+1} into the other V buffer;
+//   4. kept: online-softmax update and P to bf16; wait for the copies; B2;
+//   5. kept: O^T += V^T P^T.
+// The exponent reference max moves only when the running max has grown by
+// more than 2^8 (base-2 units), so the O/l rescale is rare; the running max
+// used by the skip decision is tracked exactly and separately.
 // ---------------------------------------------------------------------------
-template <int D, int BQ, int BK, bool PAGED>
-__global__ void __launch_bounds__(BQ * 2) fwd_bf16(FwdParams p) {
-    constexpr int NW = BQ / 32;
+constexpr float kRescaleLog2 = 8.0f;
+
+#define BSP_LDS(T, ptr) ((__attribute__((address_space(3))) T *)(ptr))
+
+// XOR swizzle of the 16-byte chunks of LDS row r (row = one key, D dims).
+template <int D>
+__device__ __forceinline__ int chunk_swz(int r) {
+    if constexpr (D == 128) return 2 * (r & 7) + ((r >> 3) & 1);
+    else return 2 * ((r >> 1) & 3);
+}
+
+__device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+template <int N>
+__device__ __forceinline__ void wait_vmem_leave() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+
+template <int D, int BQ, int BK, bool PAGED, int HPW>
+__global__ void __launch_bounds__(BQ * 2 * HPW, 1) fwd_bf16(FwdParams p) {
+    constexpr int WPH = BQ / 32;     // waves per head
+    constexpr int NW = WPH * HPW;    // waves per workgroup
     constexpr int NT = NW * 64;
-    constexpr int KS = D / 16;   // k-steps of S^T = K Q^T
-    constexpr int MT = BK / 32;  // 32-key tiles of a block
-    constexpr int DT = D / 32;   // 32-dim tiles of O^T
-    constexpr int PC = BK / 16;  // 16-key chunks of the PV contraction
-    constexpr int KSTR = D + 8;  // LDS row strides (elements), padded against bank conflicts
-    constexpr int VSTR = BK + 8;
-    __shared__ __attribute__((aligned(16))) __bf16 sK[BK * KSTR];
-    __shared__ __attribute__((aligned(16))) __bf16 sVt[D * VSTR];
+    constexpr int KS = D / 16;       // k-steps of S^T = K Q^T
+    constexpr int MT = BK / 32;      // 32-key tiles of a block
+    constexpr int DT = D / 32;       // 32-dim tiles of O^T
+    constexpr int PC = BK / 16;      // 16-key chunks of the PV contraction
+    constexpr int ROWB = D * 2;      // bytes per LDS row
+    constexpr int CPR = D / 8;       // 16-byte chunks per row
+    constexpr int BLKB = BK * ROWB;  // bytes per K or V block
+    constexpr int RPK = 1024 / ROWB; // rows per 1 KB wave copy
+    constexpr int CI = BLKB / 1024 / NW;  // copy instructions per wave per block
+    static_assert(BLKB % (1024 * NW) == 0, "block copy must split evenly over the waves");
+    __shared__ __attribute__((aligned(1024))) char sK[2][BLKB];
+    __shared__ __attribute__((aligned(1024))) char sV[2][BLKB];
     __shared__ int sVote[NW];
 
-    int s, t, h;
-    decode_item(p, s, t, h);
+    int s, t, hp;
+    decode_item(p, s, t, hp);  // hp: index of the head group served by this workgroup
     const int base = p.cu[s];
     const int L = p.cu[s + 1] - base;
     if (t * BQ >= L) return;  // tile past the end of this sequence (bitmap row stays zero)
@@ -161,24 +208,29 @@ __global__ void __launch_bounds__(BQ * 2) fwd_bf16(FwdParams p) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = tid >> 6;
-    const int ln = lane & 31;  // query (N) / key or dim (M) index inside a 32-wide MFMA tile
-    const int hh = lane >> 5;  // lane half: selects the k sub-range of MFMA operands
+    const int hl = w / WPH;            // head of this wave within the workgroup
+    const int wq = w - hl * WPH;       // wave index within its head
+    const int h = hp * HPW + hl;
+    const int ln = lane & 31;
+    const int hh = lane >> 5;
     const int g = h / p.G;
     const int r1 = min((t + 1) * BQ, L);
     const int nblk = (r1 - 1) / BK + 1;
-    const int q0 = t * BQ + w * 32;
+    const int q0 = t * BQ + wq * 32;
     const int qrow = q0 + ln;
     const bool valid = qrow < L;
     const int64_t bm_row = ((int64_t)h * p.n_seqs + s) * p.T_max + t;
+    const float c = p.c_log2;
+    const bool dense = p.lam_raw == INFINITY;
 
-    const __bf16 *qg = (const __bf16 *)p.q;
-    const __bf16 *kg = (const __bf16 *)p.k;
-    const __bf16 *vg = (const __bf16 *)p.v;
+    const __bf16 *kg = (const __bf16 *)p.k + (int64_t)g * p.k_sh;
+    const __bf16 *vg = (const __bf16 *)p.v + (int64_t)g * p.v_sh;
 
     // Q^T fragments (MFMA B operand): lane holds Q[qrow][16ks + 8hh .. +7].
     bf16x8 qf[KS];
     {
-        const __bf16 *qp = qg + (int64_t)(base + (valid ? qrow : 0)) * p.q_st + (int64_t)h * p.q_sh + 8 * hh;
+        const __bf16 *qp = (const __bf16 *)p.q + (int64_t)(base + (valid ? qrow : 0)) * p.q_st +
+                           (int64_t)h * p.q_sh + 8 * hh;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             bf16x8 x = *(const bf16x8 *)(qp + 16 * ks);
@@ -187,36 +239,54 @@ __global__ void __launch_bounds__(BQ * 2) fwd_bf16(FwdParams p) {
         }
     }
 
-    float m_run = -INFINITY;  // running max of raw scores <q,k>
+    // Copy key/value block starting at key kb into an LDS buffer. Wave w's
+    // i-th copy fills the 1 KB segment i*NW + w; lane l writes physical chunk
+    // l % CPR of row segment*RPK + l / CPR and fetches the logical chunk that
+    // the swizzle maps there. Rows past the sequence end re-read its last row
+    // (finite data, always masked).
+    auto copy_block = [&](const __bf16 *src, int64_t st, int kb, char *dst) {
+#pragma unroll
+        for (int i = 0; i < CI; ++i) {
+            const int seg = i * NW + w;
+            const int r = seg * RPK + lane / CPR;
+            const int pc = lane % CPR;
+            const int lc = pc ^ chunk_swz<D>(r);
+            const int kk = min(kb + r, L - 1);
+            const __bf16 *gp = src + kv_row<PAGED>(p, s, base, kk, st) + 8 * lc;
+            __builtin_amdgcn_global_load_lds(gp, BSP_LDS(void, dst + seg * 1024), 16, 0, 0);
+        }
+    };
+
+    float m_dec = -INFINITY;  // running max of raw scores <q,k> (skip decision)
+    float m_ref = -INFINITY;  // reference max of the exponentials (lags m_dec by < 2^8 in base 2)
     float l_run = 0.f;
     f32x16 oacc[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
     SkipLog lg;
 
+    copy_block(kg, p.k_st, 0, sK[0]);
+    if (dense) copy_block(vg, p.v_st, 0, sV[0]);
+    wait_vmem_all();
+    __syncthreads();
+
     for (int j = 0; j < nblk; ++j) {
         const int kb = j * BK;
-        __syncthreads();  // previous block's LDS reads are done
-        // ---- K block -> LDS, row-major [key][dim]
-#pragma unroll
-        for (int c = tid; c < BK * D / 8; c += NT) {
-            const int r = c / (D / 8);
-            const int c8 = c % (D / 8);
-            const int kk = kb + r;
-            bf16x8 x{};
-            if (kk < L) x = *(const bf16x8 *)(kg + kv_row<PAGED>(p, s, base, kk, p.k_st) + (int64_t)g * p.k_sh + 8 * c8);
-            *(bf16x8 *)&sK[r * KSTR + 8 * c8] = x;
-        }
-        __syncthreads();
+        const int cur = j & 1;
+        const bool has_next = j + 1 < nblk;
+        if (has_next) copy_block(kg, p.k_st, kb + BK, sK[cur ^ 1]);
 
         // ---- S^T = K Q^T : sacc[mt] holds keys 32mt + 8(i/4) + 4hh + i%4 for query qrow
+        const char *kbuf = sK[cur];
         f32x16 sacc[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
+            const int r = 32 * mt + ln;
+            const int sw = chunk_swz<D>(r);
             f32x16 acc{};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8 a = *(const bf16x8 *)&sK[(32 * mt + ln) * KSTR + 16 * ks + 8 * hh];
+                const bf16x8 a = *(const bf16x8 *)(kbuf + r * ROWB + (((2 * ks + hh) ^ sw) << 4));
                 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], acc, 0, 0, 0);
             }
             sacc[mt] = acc;
@@ -237,99 +307,94 @@ __global__ void __launch_bounds__(BQ * 2) fwd_bf16(FwdParams p) {
         for (int mt = 1; mt < MT; ++mt) mloc = fmaxf(mloc, wave_max16(sacc[mt]));
         mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
 
-        // ---- skip decision: every valid row must have gap > lambda
-        const bool ok = !valid || (mloc == -INFINITY) || (m_run - mloc > p.lam_raw);
-        const int wall = __all(ok);
-        if (lane == 0) sVote[w] = wall;
-        __syncthreads();
-        bool skip = true;
+        // ---- skip decision: every valid row of the head's tile must have gap > lambda
+        bool skip = false;
+        if (!dense) {
+            const bool ok = !valid || (mloc == -INFINITY) || (m_dec - mloc > p.lam_raw);
+            const int wall = __all(ok);
+            if (lane == 0) sVote[w] = wall;
+        }
+        __syncthreads();  // B1: votes visible; every wave is done with PV_{j-1} and QK_j
+        if (!dense) {
+            bool any_keep = false;
 #pragma unroll
-        for (int x = 0; x < NW; ++x) skip = skip && (sVote[x] != 0);
-        log_decision(p, lg, bm_row, j, nblk, skip);
-        if (skip) continue;  // no exp, no V load, no PV
-
-        // ---- issue the V loads for this kept block (8x8 sub-blocks per thread)
-        constexpr int NSB = (BK / 8) * (D / 8);
-        constexpr int SBT = (NSB + NT - 1) / NT;
-        u32x4 vraw[SBT][8];
+            for (int x = 0; x < HPW; ++x) {
+                bool sk = true;
 #pragma unroll
-        for (int it = 0; it < SBT; ++it) {
-            const int sb = tid + it * NT;
-            const int kgl = sb & 7;
-            const int dgi = (sb >> 3) % (D / 8);
-            const int kgh = (sb >> 3) / (D / 8);
-            const int kgrp = kgh * 8 + kgl;
-#pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                const int kk = kb + 8 * kgrp + r;
-                u32x4 x{};
-                if (sb < NSB && kk < L)
-                    x = *(const u32x4 *)(vg + kv_row<PAGED>(p, s, base, kk, p.v_st) + (int64_t)g * p.v_sh + 8 * dgi);
-                vraw[it][r] = x;
+                for (int y = 0; y < WPH; ++y) sk = sk && (sVote[x * WPH + y] != 0);
+                if (x == hl) skip = sk;
+                any_keep = any_keep || !sk;
             }
+            if (any_keep) copy_block(vg, p.v_st, kb, sV[cur]);
+            if (wq == 0) log_decision(p, lg, bm_row, j, nblk, skip, lane == 0);
+        } else if (has_next) {
+            copy_block(vg, p.v_st, kb + BK, sV[cur ^ 1]);
         }
 
-        // ---- online softmax update (exp2 with the scale folded in)
-        const float m_new = fmaxf(m_run, mloc);
-        const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_run - m_new) * p.c_log2);
-        const float mc = m_new * p.c_log2;
-        float rs = 0.f;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float e = __builtin_amdgcn_exp2f(fmaf(sacc[mt][i], p.c_log2, -mc));
-                sacc[mt][i] = e;
-                rs += e;
-            }
-        rs += __shfl_xor(rs, 32);
-        l_run = alpha * l_run + rs;
-        m_run = m_new;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
         bf16x8 pb[PC];
+        if (!skip) {
+            // ---- online softmax update (exp2 with the scale folded in)
+            const float m_new = fmaxf(m_dec, mloc);
+            m_dec = m_new;
+            const bool need = (m_new - m_ref) * c > kRescaleLog2;  // also true while m_ref = -inf
+            if (__any(need)) {
+                const float alpha =
+                    need ? ((m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_ref - m_new) * c)) : 1.f;
+                if (need) m_ref = m_new;
+                l_run *= alpha;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int u = 0; u < 2; ++u)
-#pragma unroll
-                for (int i = 0; i < 8; ++i) pb[2 * mt + u][i] = (__bf16)sacc[mt][8 * u + i];
-
-        // ---- transpose the V sub-blocks into LDS as V^T [dim][key]
-#pragma unroll
-        for (int it = 0; it < SBT; ++it) {
-            const int sb = tid + it * NT;
-            if (sb < NSB) {
-                const int kgl = sb & 7;
-                const int dgi = (sb >> 3) % (D / 8);
-                const int kgh = (sb >> 3) / (D / 8);
-                const int kgrp = kgh * 8 + kgl;
-#pragma unroll
-                for (int dd = 0; dd < 8; ++dd) {
-                    u32x4 out;
-#pragma unroll
-                    for (int c2 = 0; c2 < 4; ++c2) {
-                        const uint32_t x = vraw[it][2 * c2][dd >> 1];
-                        const uint32_t y = vraw[it][2 * c2 + 1][dd >> 1];
-                        out[c2] = (dd & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
-                    }
-                    *(u32x4 *)&sVt[(8 * dgi + dd) * VSTR + 8 * kgrp] = out;
-                }
+                for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
             }
+            const float mc = m_ref * c;
+            float rs = 0.f;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const float e = __builtin_amdgcn_exp2f(fmaf(sacc[mt][i], c, -mc));
+                    sacc[mt][i] = e;
+                    rs += e;
+                }
+            rs += __shfl_xor(rs, 32);
+            l_run += rs;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) pb[2 * mt + u][i] = (__bf16)sacc[mt][8 * u + i];
         }
+        // B2: K_{j+1} and V_j are in LDS. Loads complete in issue order, so in dense mode the
+        // copy of V_{j+1} (issued last) may stay in flight across the barrier.
+        if (dense && has_next) wait_vmem_leave<CI>();
+        else wait_vmem_all();
         __syncthreads();
 
-        // ---- O^T += V^T P^T ; contraction chunk c covers keys 32mt + 16u + {0..3, 8..11} + 4hh
+        if (!skip) {
+            // ---- O^T += V^T P^T. Contraction chunk cc covers keys 32mt + 16u + 8(i'/4) + 4hh + i'%4
+            // (i' = 0..7). Two transposing reads give lane (dim d, half hh) those 8 keys: in each
+            // 16-lane group, source lane i points at key base + 4hh + i/4 (+8), dims 4(i%4)..+3.
+            const char *vbuf = sV[cur];
+            const int grp = lane >> 4;
+            const int gi = lane & 15;
+            const int ghh = grp >> 1;
+            const int dsub = 16 * (grp & 1) + 4 * (gi & 3);
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            const __bf16 *vr = &sVt[(32 * dt + ln) * VSTR];
+            for (int dt = 0; dt < DT; ++dt) {
+                const int d = 32 * dt + dsub;
+                const int lch = d >> 3;
+                const int off = (d & 7) * 2;
 #pragma unroll
-            for (int c = 0; c < PC; ++c) {
-                const int k0 = 32 * (c >> 1) + 16 * (c & 1) + 4 * hh;
-                const bf16x4 lo = *(const bf16x4 *)(vr + k0);
-                const bf16x4 hi = *(const bf16x4 *)(vr + k0 + 8);
-                const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[c], oacc[dt], 0, 0, 0);
+                for (int cc = 0; cc < PC; ++cc) {
+                    const int r0 = 32 * (cc >> 1) + 16 * (cc & 1) + 4 * ghh + (gi >> 2);
+                    const int r8 = r0 + 8;
+                    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                        BSP_LDS(bf16x4, vbuf + r0 * ROWB + ((lch ^ chunk_swz<D>(r0)) << 4) + off));
+                    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                        BSP_LDS(bf16x4, vbuf + r8 * ROWB + ((lch ^ chunk_swz<D>(r8)) << 4) + off));
+                    const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                    oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[cc], oacc[dt], 0, 0, 0);
+                }
             }
         }
     }
@@ -347,9 +412,9 @@ __global__ void __launch_bounds__(BQ * 2) fwd_bf16(FwdParams p) {
                 *(bf16x4 *)(op + 32 * dt + 8 * g4 + 4 * hh) = x;
             }
         if (hh == 0 && p.lse != nullptr)
-            p.lse[(int64_t)h * p.lse_sh + base + qrow] = (m_run * p.c_log2 + __log2f(l_run)) * kLn2;
+            p.lse[(int64_t)h * p.lse_sh + base + qrow] = (m_ref * c + __log2f(l_run)) * kLn2;
     }
-    if (tid == 0) {
+    if (wq == 0 && lane == 0) {
         if (p.skip_count) atomicAdd(&p.skip_count[h], (unsigned long long)lg.nskip);
         if (p.visited_count) atomicAdd(&p.visited_count[h], (unsigned long long)nblk);
     }
@@ -451,7 +516,7 @@ __global__ void __launch_bounds__(BQ * 2) fwd_f32(FwdParams p) {
         bool skip = true;
 #pragma unroll
         for (int x = 0; x < NW; ++x) skip = skip && (sVote[x] != 0);
-        log_decision(p, lg, bm_row, j, nblk, skip);
+        log_decision(p, lg, bm_row, j, nblk, skip, tid == 0);
         if (skip) continue;
 
         for (int c = tid; c < BK * D / 4; c += NT) {
@@ -564,15 +629,22 @@ bsp_status_t check_tensor(const char *name, const bsp_tensor_t *x, int heads, in
 typedef void (*kernel_fn)(FwdParams);
 
 template <int D, int BQ, int BK>
-kernel_fn pick_kernel(int dtype, bool paged) {
-    if (dtype == BSP_BF16) return paged ? fwd_bf16<D, BQ, BK, true> : fwd_bf16<D, BQ, BK, false>;
+kernel_fn pick_kernel(int dtype, bool paged, int hpw) {
+    if (dtype == BSP_BF16) {
+        if (hpw == 2) return paged ? fwd_bf16<D, BQ, BK, true, 2> : fwd_bf16<D, BQ, BK, false, 2>;
+        return paged ? fwd_bf16<D, BQ, BK, true, 1> : fwd_bf16<D, BQ, BK, false, 1>;
+    }
     if (dtype == BSP_F32) return paged ? fwd_f32<D, BQ, BK, true> : fwd_f32<D, BQ, BK, false>;
     return nullptr;
 }
 
-kernel_fn find_kernel(int dtype, int D, int BQ, int BK, bool paged) {
+// Query heads per workgroup: bf16 kernels pair the query heads of a KV head
+// when the group size is even.
+int heads_per_workgroup(int dtype, int group) { return (dtype == BSP_BF16 && group % 2 == 0) ? 2 : 1; }
+
+kernel_fn find_kernel(int dtype, int D, int BQ, int BK, bool paged, int hpw) {
 #define BSP_CASE(d, bq, bk) \
-    if (D == d && BQ == bq && BK == bk) return pick_kernel<d, bq, bk>(dtype, paged);
+    if (D == d && BQ == bq && BK == bk) return pick_kernel<d, bq, bk>(dtype, paged, hpw);
     BSP_CASE(64, 64, 64)
     BSP_CASE(64, 128, 64)
     BSP_CASE(64, 128, 128)
@@ -687,9 +759,10 @@ bsp_status_t bsp_attn_fwd(const bsp_tensor_t *q, const bsp_tensor_t *k, const bs
             return fail(BSP_ERR_INVALID_ARG, "bitmap holds %lld words, %lld needed", (long long)skip_out->bitmap_words,
                         (long long)words);
     }
-    const int64_t grid64 = T_max * (int64_t)seqs->n_seqs * n_heads_q;
+    const int hpw = heads_per_workgroup(q->dtype, n_heads_q / n_heads_kv);
+    const int64_t grid64 = T_max * (int64_t)seqs->n_seqs * (n_heads_q / hpw);
     if (grid64 > 0x7fffffffLL) return fail(BSP_ERR_INVALID_ARG, "too many work items");
-    kernel_fn fn = find_kernel(q->dtype, head_dim, block_q, block_k, paged);
+    kernel_fn fn = find_kernel(q->dtype, head_dim, block_q, block_k, paged, hpw);
     if (fn == nullptr)
         return fail(BSP_ERR_UNSUPPORTED, "no kernel for dtype %d, head_dim %d, block_q %d, block_k %d", (int)q->dtype,
                     head_dim, block_q, block_k);
@@ -736,10 +809,11 @@ bsp_status_t bsp_attn_fwd(const bsp_tensor_t *q, const bsp_tensor_t *k, const bs
         p.Hkv = n_heads_kv;
         p.G = n_heads_q / n_heads_kv;
         p.xcd_mode = (n_heads_kv % 8 == 0) ? 1 : 0;
+        p.hpw = hpw;
         const double scale = 1.0 / sqrt((double)head_dim);
         p.c_log2 = (float)(scale * 1.4426950408889634);
         p.lam_raw = isinf(lambda) ? INFINITY : (float)((double)lambda / scale);
-        hipLaunchKernelGGL(fn, dim3((unsigned)grid64), dim3(block_q * 2), 0, hs, p);
+        hipLaunchKernelGGL(fn, dim3((unsigned)grid64), dim3(block_q * 2 * hpw), 0, hs, p);
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(BSP_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
