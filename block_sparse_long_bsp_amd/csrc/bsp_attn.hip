@@ -71,6 +71,8 @@ struct FwdParams {
 
 constexpr float kLn2 = 0.69314718055994530942f;
 
+#define BSP_LDS(T, ptr) ((__attribute__((address_space(3))) T *)(ptr))
+
 // Map the workgroup id to (sequence, query tile, head group of HPW query heads
 // that share one KV head). Tiles are dealt from the last (heaviest under the
 // causal mask) to the first; in XCD mode the head groups of KV head x + 8i
@@ -152,22 +154,20 @@ __device__ __forceinline__ void log_decision(const FwdParams &p, SkipLog &lg, in
 // PV operand reads (ds_read_b64_tr_b16, which hands each lane four keys of one
 // dim) are free of bank conflicts.
 //
-// Per key block j:
+// Per key block j (software-pipelined: the PV product of a kept block runs one
+// block later, interleaved with the next block's softmax):
 //   1. start the copy of K_{j+1} into the other K buffer;
 //   2. S^T = K_j Q^T; causal mask on the diagonal block; row maxima; per-head
-//      vote; barrier B1;
-//   3. sparse mode: start the copy of V_j only if some head keeps block j;
-//      dense mode (lambda = +inf, nothing can be skipped): start the copy of
-//      V_{j+1} into the other V buffer;
-//   4. kept: online-softmax update and P to bf16; wait for the copies; B2;
-//   5. kept: O^T += V^T P^T.
+//      vote; barrier B1 (which also publishes V_{j-1});
+//   3. start the copy of V_j into its buffer only if some head keeps block j
+//      (with lambda = +inf every block is kept and there is no vote);
+//   4. softmax of block j (if kept) while O^T += V^T P^T of the previous kept
+//      block runs from the other V buffer; barrier B2 publishes K_{j+1}.
 // The exponent reference max moves only when the running max has grown by
 // more than 2^8 (base-2 units), so the O/l rescale is rare; the running max
 // used by the skip decision is tracked exactly and separately.
 // ---------------------------------------------------------------------------
 constexpr float kRescaleLog2 = 8.0f;
-
-#define BSP_LDS(T, ptr) ((__attribute__((address_space(3))) T *)(ptr))
 
 // XOR swizzle of the 16-byte chunks of LDS row r (row = one key, D dims).
 template <int D>
@@ -177,6 +177,16 @@ __device__ __forceinline__ int chunk_swz(int r) {
 }
 
 __device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// 16-byte global -> LDS copy for the whole wave: lane l's 16 bytes from `gptr`
+// land at LDS byte address lds + 16 l (lds must be wave-uniform). Issued from
+// inline assembly so that the compiler does not serialise it against unrelated
+// LDS reads; completion is awaited explicitly (s_waitcnt vmcnt) before the
+// barrier that publishes the buffer.
+__device__ __forceinline__ void lds_copy16(const void *gptr, const void *lds) {
+    const uint32_t la = (uint32_t)(uintptr_t)BSP_LDS(const void, lds);
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(la) : "m0");
+}
 template <int N>
 __device__ __forceinline__ void wait_vmem_leave() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 
@@ -207,7 +217,7 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, 1) fwd_bf16(FwdParams p) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int w = tid >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform: keeps wave data in SGPRs)
     const int hl = w / WPH;            // head of this wave within the workgroup
     const int wq = w - hl * WPH;       // wave index within its head
     const int h = hp * HPW + hl;
@@ -239,21 +249,36 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, 1) fwd_bf16(FwdParams p) {
         }
     }
 
-    // Copy key/value block starting at key kb into an LDS buffer. Wave w's
+    // Copy the key/value block starting at key kb into an LDS buffer. Wave w's
     // i-th copy fills the 1 KB segment i*NW + w; lane l writes physical chunk
     // l % CPR of row segment*RPK + l / CPR and fetches the logical chunk that
     // the swizzle maps there. Rows past the sequence end re-read its last row
-    // (finite data, always masked).
-    auto copy_block = [&](const __bf16 *src, int64_t st, int kb, char *dst) {
+    // (finite data, always masked). For packed K/V the per-lane element offset
+    // inside a block is fixed, so it is computed once.
+    // Copy i covers rows crow0 + i*CSTEP. When CSTEP is a multiple of the swizzle period (16
+    // rows) the logical chunk is the same for every copy and the in-block element offset is
+    // crow0*stride + chunk + i*CSTEP*stride; otherwise the chunk is recomputed per copy.
+    constexpr int CSTEP = NW * RPK;
+    constexpr bool kFixedChunk = CSTEP % 16 == 0;
+    const int crow0 = w * RPK + lane / CPR;
+    const int lc8 = 8 * ((lane % CPR) ^ chunk_swz<D>(crow0));
+    const int kofs0 = (int)(crow0 * p.k_st) + lc8;
+    const int vofs0 = (int)(crow0 * p.v_st) + lc8;
+    auto copy_block = [&](const __bf16 *src, int64_t st, int ofs0, int kb, char *dst) {
+        if (!PAGED && kFixedChunk && kb + BK <= L) {
+            const __bf16 *blk = src + (int64_t)(base + kb) * st + ofs0;
 #pragma unroll
-        for (int i = 0; i < CI; ++i) {
-            const int seg = i * NW + w;
-            const int r = seg * RPK + lane / CPR;
-            const int pc = lane % CPR;
-            const int lc = pc ^ chunk_swz<D>(r);
-            const int kk = min(kb + r, L - 1);
-            const __bf16 *gp = src + kv_row<PAGED>(p, s, base, kk, st) + 8 * lc;
-            __builtin_amdgcn_global_load_lds(gp, BSP_LDS(void, dst + seg * 1024), 16, 0, 0);
+            for (int i = 0; i < CI; ++i)
+                lds_copy16(blk + (int64_t)(i * CSTEP) * st, dst + (i * NW + w) * 1024);
+        } else {
+#pragma unroll
+            for (int i = 0; i < CI; ++i) {
+                const int r = crow0 + i * CSTEP;
+                const int kk = min(kb + r, L - 1);
+                const int lci8 = kFixedChunk ? lc8 : 8 * ((lane % CPR) ^ chunk_swz<D>(r));
+                const __bf16 *gp = src + kv_row<PAGED>(p, s, base, kk, st) + lci8;
+                lds_copy16(gp, dst + (i * NW + w) * 1024);
+            }
         }
     };
 
@@ -265,31 +290,73 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, 1) fwd_bf16(FwdParams p) {
     for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
     SkipLog lg;
 
-    copy_block(kg, p.k_st, 0, sK[0]);
-    if (dense) copy_block(vg, p.v_st, 0, sV[0]);
+    // K operand reads: row 32mt + ln (the swizzle repeats every 16 rows, so it is that of row ln).
+    const int krow = ln * ROWB;
+    const int ksw = chunk_swz<D>(ln);
+
+    // PV operand reads: contraction chunk cc = 2mt + u covers keys 32mt + 16u + 8(i'/4) + 4hh + i'%4
+    // (i' = 0..7). Two transposing reads give lane (dim d, half hh) those 8 keys: in each 16-lane
+    // group, source lane i points at key 32mt + 16u + 4hh + i/4 (+8), dims d0 + 4(i%4)..+3. The
+    // swizzle depends on the key only through key % 16, which is the same for every mt.
+    // The second read (keys +8) differs only in the swizzle bit (D = 128) or not at all (D = 64).
+    int vrd_off[2][DT];
+    {
+        const int grp = lane >> 4;
+        const int gi = lane & 15;
+        const int dsub = 16 * (grp & 1) + 4 * (gi & 3);
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const int d = 32 * dt + dsub;
+                const int r0 = 16 * u + 4 * (grp >> 1) + (gi >> 2);
+                vrd_off[u][dt] = r0 * ROWB + (((d >> 3) ^ chunk_swz<D>(r0)) << 4) + (d & 7) * 2;
+            }
+    }
+
+    // O^T += V^T P^T for a kept block whose bf16 probabilities are in pp and whose V is in vbuf.
+    auto pv_block = [&](const bf16x8 *pp, const char *vbuf) {
+#pragma unroll
+        for (int cc = 0; cc < PC; ++cc) {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const int o0 = vrd_off[cc & 1][dt] + (cc >> 1) * 32 * ROWB;
+                const int o8 = (D == 128 ? (o0 ^ 16) : o0) + 8 * ROWB;
+                const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(BSP_LDS(bf16x4, vbuf + o0));
+                const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(BSP_LDS(bf16x4, vbuf + o8));
+                const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pp[cc], oacc[dt], 0, 0, 0);
+            }
+        }
+    };
+
+    copy_block(kg, p.k_st, kofs0, 0, sK[0]);
     wait_vmem_all();
     __syncthreads();
+
+    bf16x8 pprev[PC];       // probabilities of this wave's last kept block, PV still pending
+    bool pend = false;      // wave-uniform: a PV is pending
+    bool v_prev = false;    // workgroup-uniform: V of block j-1 was copied
 
     for (int j = 0; j < nblk; ++j) {
         const int kb = j * BK;
         const int cur = j & 1;
         const bool has_next = j + 1 < nblk;
-        if (has_next) copy_block(kg, p.k_st, kb + BK, sK[cur ^ 1]);
+        if (has_next) copy_block(kg, p.k_st, kofs0, kb + BK, sK[cur ^ 1]);
 
-        // ---- S^T = K Q^T : sacc[mt] holds keys 32mt + 8(i/4) + 4hh + i%4 for query qrow
+        // ---- S^T = K Q^T : sacc[mt] holds keys 32mt + 8(i/4) + 4hh + i%4 for query qrow.
+        // The k-step loop is outermost so that consecutive MFMAs use independent accumulators.
         const char *kbuf = sK[cur];
         f32x16 sacc[MT];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const int r = 32 * mt + ln;
-            const int sw = chunk_swz<D>(r);
-            f32x16 acc{};
+        for (int mt = 0; mt < MT; ++mt) sacc[mt] = f32x16{};
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8 a = *(const bf16x8 *)(kbuf + r * ROWB + (((2 * ks + hh) ^ sw) << 4));
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], acc, 0, 0, 0);
+        for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const bf16x8 a = *(const bf16x8 *)(kbuf + krow + 32 * mt * ROWB + (((2 * ks + hh) ^ ksw) << 4));
+                sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sacc[mt], 0, 0, 0);
             }
-            sacc[mt] = acc;
         }
         // ---- causal mask (only where the block reaches past this wave's first query)
         if (kb + BK - 1 > q0) {
@@ -308,15 +375,21 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, 1) fwd_bf16(FwdParams p) {
         mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
 
         // ---- skip decision: every valid row of the head's tile must have gap > lambda
-        bool skip = false;
         if (!dense) {
             const bool ok = !valid || (mloc == -INFINITY) || (m_dec - mloc > p.lam_raw);
             const int wall = __all(ok);
             if (lane == 0) sVote[w] = wall;
         }
-        __syncthreads();  // B1: votes visible; every wave is done with PV_{j-1} and QK_j
+        // V_{j-1} (copied during the previous block) must be in LDS before B1; K_{j+1} may still fly.
+        if (v_prev) {
+            if (has_next) wait_vmem_leave<CI>();
+            else wait_vmem_all();
+        }
+        __syncthreads();  // B1: votes and V_{j-1} visible; every wave is done with QK_j
+        bool skip = false;
+        bool any_keep = true;
         if (!dense) {
-            bool any_keep = false;
+            any_keep = false;
 #pragma unroll
             for (int x = 0; x < HPW; ++x) {
                 bool sk = true;
@@ -325,79 +398,62 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, 1) fwd_bf16(FwdParams p) {
                 if (x == hl) skip = sk;
                 any_keep = any_keep || !sk;
             }
-            if (any_keep) copy_block(vg, p.v_st, kb, sV[cur]);
             if (wq == 0) log_decision(p, lg, bm_row, j, nblk, skip, lane == 0);
-        } else if (has_next) {
-            copy_block(vg, p.v_st, kb + BK, sV[cur ^ 1]);
         }
+        if (any_keep) copy_block(vg, p.v_st, vofs0, kb, sV[cur]);
 
-        bf16x8 pb[PC];
+        // ---- softmax of block j, overlapped with the pending PV of the previous kept block
+        float alpha = 1.f;
+        bool resc = false;
         if (!skip) {
-            // ---- online softmax update (exp2 with the scale folded in)
             const float m_new = fmaxf(m_dec, mloc);
             m_dec = m_new;
             const bool need = (m_new - m_ref) * c > kRescaleLog2;  // also true while m_ref = -inf
-            if (__any(need)) {
-                const float alpha =
-                    need ? ((m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_ref - m_new) * c)) : 1.f;
-                if (need) m_ref = m_new;
-                l_run *= alpha;
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+            resc = __any(need);
+            if (need) {
+                alpha = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_ref - m_new) * c);
+                m_ref = m_new;
             }
             const float mc = m_ref * c;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) sacc[mt][i] = __builtin_amdgcn_exp2f(fmaf(sacc[mt][i], c, -mc));
+        }
+        if (pend) pv_block(pprev, sV[cur ^ 1]);
+        if (!skip) {
             float rs = 0.f;
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const float e = __builtin_amdgcn_exp2f(fmaf(sacc[mt][i], c, -mc));
-                    sacc[mt][i] = e;
-                    rs += e;
-                }
+                for (int i = 0; i < 16; ++i) rs += sacc[mt][i];
             rs += __shfl_xor(rs, 32);
+            if (resc) {  // after the pending PV: O and l are then both relative to the new reference
+                l_run *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+            }
             l_run += rs;
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                 for (int u = 0; u < 2; ++u)
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) pb[2 * mt + u][i] = (__bf16)sacc[mt][8 * u + i];
+                    for (int i = 0; i < 8; ++i) pprev[2 * mt + u][i] = (__bf16)sacc[mt][8 * u + i];
         }
-        // B2: K_{j+1} and V_j are in LDS. Loads complete in issue order, so in dense mode the
-        // copy of V_{j+1} (issued last) may stay in flight across the barrier.
-        if (dense && has_next) wait_vmem_leave<CI>();
+        pend = !skip;
+        v_prev = any_keep;
+
+        // B2: K_{j+1} is in LDS (loads complete in issue order; V_j, issued last, may still fly).
+        if (any_keep) wait_vmem_leave<CI>();
         else wait_vmem_all();
         __syncthreads();
-
-        if (!skip) {
-            // ---- O^T += V^T P^T. Contraction chunk cc covers keys 32mt + 16u + 8(i'/4) + 4hh + i'%4
-            // (i' = 0..7). Two transposing reads give lane (dim d, half hh) those 8 keys: in each
-            // 16-lane group, source lane i points at key base + 4hh + i/4 (+8), dims 4(i%4)..+3.
-            const char *vbuf = sV[cur];
-            const int grp = lane >> 4;
-            const int gi = lane & 15;
-            const int ghh = grp >> 1;
-            const int dsub = 16 * (grp & 1) + 4 * (gi & 3);
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                const int d = 32 * dt + dsub;
-                const int lch = d >> 3;
-                const int off = (d & 7) * 2;
-#pragma unroll
-                for (int cc = 0; cc < PC; ++cc) {
-                    const int r0 = 32 * (cc >> 1) + 16 * (cc & 1) + 4 * ghh + (gi >> 2);
-                    const int r8 = r0 + 8;
-                    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                        BSP_LDS(bf16x4, vbuf + r0 * ROWB + ((lch ^ chunk_swz<D>(r0)) << 4) + off));
-                    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                        BSP_LDS(bf16x4, vbuf + r8 * ROWB + ((lch ^ chunk_swz<D>(r8)) << 4) + off));
-                    const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                    oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[cc], oacc[dt], 0, 0, 0);
-                }
-            }
-        }
     }
+    if (v_prev) {
+        wait_vmem_all();
+        __syncthreads();
+    }
+    if (pend) pv_block(pprev, sV[(nblk - 1) & 1]);
 
     // ---- epilogue: normalise, store O (bf16) and LSE (natural log)
     if (valid) {
