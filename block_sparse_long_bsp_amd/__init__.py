@@ -21,7 +21,8 @@ from typing import Optional, Tuple
 import torch  # must be imported before the library so both share one HIP runtime
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libbsp_attn.so")
+# BSP_ATTN_LIB may point at another build of the same library (A/B measurements).
+LIB_PATH = os.environ.get("BSP_ATTN_LIB") or os.path.join(_PKG, "libbsp_attn.so")
 
 BSP_OK, BSP_ERR_INVALID_ARG, BSP_ERR_UNSUPPORTED, BSP_ERR_HIP, BSP_ERR_DEVICE = range(5)
 BSP_F32, BSP_BF16, BSP_FP8_E4M3 = 0, 1, 2
