@@ -34,6 +34,7 @@
 #include <string.h>
 
 #include <mutex>
+#include <type_traits>
 
 #include "bsp_attn.h"
 
@@ -67,6 +68,11 @@ struct FwdParams {
     int32_t hpw;                    // query heads per workgroup (divides G)
     float c_log2;                   // softmax scale * log2(e)
     float lam_raw;                  // lambda in raw dot-product units (lambda / scale)
+    // fp8 inputs: per-head dequantisation scales (device, float); the kernel folds
+    // q_scale[h] * k_scale[g] into its score scale and v_scale[g] into the output.
+    const float *q_scale, *k_scale, *v_scale;
+    float scale;                    // 1 / sqrt(head_dim)
+    float lam;                      // lambda in natural-log units (+inf: dense)
 };
 
 constexpr float kLn2 = 0.69314718055994530942f;
@@ -143,7 +149,15 @@ __device__ __forceinline__ void log_decision(const FwdParams &p, SkipLog &lg, in
 }
 
 // ---------------------------------------------------------------------------
-// bf16 kernel: QK^T and PV on v_mfma_f32_32x32x16_bf16, fp32 accumulation.
+// MFMA kernel for bf16 and fp8 e4m3 inputs, fp32 accumulation.
+//
+//   bf16: S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_32x32x16_bf16.
+//   fp8 : S^T = K Q^T on v_mfma_f32_32x32x64_f8f6f4 (e4m3 x e4m3, per-head
+//         dequantisation scales folded into the score scale); V is widened
+//         from e4m3 to bf16 (exact) once per block in LDS and O^T = V^T P^T
+//         runs on the bf16 MFMA with bf16 probabilities. Probabilities rounded
+//         to e4m3 (3 mantissa bits) would cost up to ~6% of the dominant
+//         term of a peaked row, too coarse for the output tolerance.
 //
 // A workgroup serves one query tile of HPW query heads that share a KV head
 // (GQA grouping), with block_q/32 waves per head; K and V blocks are staged
@@ -158,23 +172,35 @@ __device__ __forceinline__ void log_decision(const FwdParams &p, SkipLog &lg, in
 // block later, interleaved with the next block's softmax):
 //   1. start the copy of K_{j+1} into the other K buffer;
 //   2. S^T = K_j Q^T; causal mask on the diagonal block; row maxima; per-head
-//      vote; barrier B1 (which also publishes V_{j-1});
-//   3. start the copy of V_j into its buffer only if some head keeps block j
-//      (with lambda = +inf every block is kept and there is no vote);
+//      vote; (fp8: widen the staged V_{j-1} into the bf16 V buffer); barrier
+//      B1 (which also publishes V_{j-1});
+//   3. start the copy of V_j (bf16: into its buffer; fp8: into the staging
+//      buffer) only if some head keeps block j (with lambda = +inf every block
+//      is kept and there is no vote);
 //   4. softmax of block j (if kept) while O^T += V^T P^T of the previous kept
-//      block runs from the other V buffer; barrier B2 publishes K_{j+1}.
+//      block runs from the V buffer; barrier B2 publishes K_{j+1}.
 // The exponent reference max moves only when the running max has grown by
 // more than 2^8 (base-2 units), so the O/l rescale is rare; the running max
 // used by the skip decision is tracked exactly and separately.
 // ---------------------------------------------------------------------------
 constexpr float kRescaleLog2 = 8.0f;
 
-// XOR swizzle of the 16-byte chunks of LDS row r (row = one key, D dims).
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// XOR swizzle of the 16-byte chunks of a bf16 LDS row r (row = one key, 2*D bytes).
 template <int D>
 __device__ __forceinline__ int chunk_swz(int r) {
     if constexpr (D == 128) return 2 * (r & 7) + ((r >> 3) & 1);
     else return 2 * ((r >> 1) & 3);
 }
+
+// XOR swizzle of the 16-byte chunks of an fp8 K row r (128 bytes: two rows per
+// 256-byte bank window). The eight rows of equal parity among sixteen
+// consecutive rows get eight distinct chunk XORs, so the sixteen lanes that
+// one ds_read_b128 cycle serves (rows 0..15 of a tile, one logical chunk) hit
+// sixteen distinct 16-byte bank groups.
+__device__ __forceinline__ int chunk_swz8(int r) { return (r >> 1) & 7; }
 
 __device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -190,23 +216,37 @@ __device__ __forceinline__ void lds_copy16(const void *gptr, const void *lds) {
 template <int N>
 __device__ __forceinline__ void wait_vmem_leave() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 
-template <int D, int BQ, int BK, bool PAGED, int HPW>
-__global__ void __launch_bounds__(BQ * 2 * HPW, 1) fwd_bf16(FwdParams p) {
+// Two e4m3 codes (bytes 2*HI and 2*HI+1 of x) widened to bf16; exact, since
+// every e4m3 value (subnormals included) is a bf16 value.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t x) {
+    const bf16x2 y = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, HI);
+    return __builtin_bit_cast(uint32_t, y);
+}
+
+template <int IN, int D, int BQ, int BK, bool PAGED, int HPW>
+__global__ void __launch_bounds__(BQ * 2 * HPW, 1) fwd_mfma(FwdParams p) {
+    constexpr bool F8 = IN == BSP_FP8_E4M3;
     constexpr int WPH = BQ / 32;     // waves per head
     constexpr int NW = WPH * HPW;    // waves per workgroup
-    constexpr int NT = NW * 64;
-    constexpr int KS = D / 16;       // k-steps of S^T = K Q^T
+    constexpr int ES = F8 ? 1 : 2;   // bytes per input element
+    constexpr int KS = F8 ? D / 64 : D / 16;  // k-steps of S^T = K Q^T
     constexpr int MT = BK / 32;      // 32-key tiles of a block
     constexpr int DT = D / 32;       // 32-dim tiles of O^T
     constexpr int PC = BK / 16;      // 16-key chunks of the PV contraction
-    constexpr int ROWB = D * 2;      // bytes per LDS row
-    constexpr int CPR = D / 8;       // 16-byte chunks per row
-    constexpr int BLKB = BK * ROWB;  // bytes per K or V block
-    constexpr int RPK = 1024 / ROWB; // rows per 1 KB wave copy
-    constexpr int CI = BLKB / 1024 / NW;  // copy instructions per wave per block
-    static_assert(BLKB % (1024 * NW) == 0, "block copy must split evenly over the waves");
-    __shared__ __attribute__((aligned(1024))) char sK[2][BLKB];
-    __shared__ __attribute__((aligned(1024))) char sV[2][BLKB];
+    constexpr int KROWB = D * ES;    // bytes per LDS row of K (and of the fp8 V staging buffer)
+    constexpr int KCPR = KROWB / 16; // 16-byte chunks per such row
+    constexpr int KBLKB = BK * KROWB;
+    constexpr int KRPK = 1024 / KROWB;  // rows per 1 KB wave copy
+    constexpr int CI = KBLKB / 1024 / NW;  // copy instructions per wave per block
+    constexpr int VROWB = D * 2;     // bytes per LDS row of V (bf16 for both input types)
+    constexpr int VBLKB = BK * VROWB;
+    constexpr int NVB = F8 ? 1 : 2;  // bf16 V buffers (fp8: widened in a phase of its own, one buffer)
+    static_assert(KBLKB % (1024 * NW) == 0, "block copy must split evenly over the waves");
+    static_assert(!F8 || D == 128, "fp8 kernels are built for head_dim 128");
+    __shared__ __attribute__((aligned(1024))) char sK[2][KBLKB];
+    __shared__ __attribute__((aligned(1024))) char sV[NVB][VBLKB];
+    __shared__ __attribute__((aligned(1024))) char sV8[F8 ? KBLKB : 16];  // fp8 V staging
     __shared__ int sVote[NW];
 
     int s, t, hp;
@@ -230,54 +270,97 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, 1) fwd_bf16(FwdParams p) {
     const int qrow = q0 + ln;
     const bool valid = qrow < L;
     const int64_t bm_row = ((int64_t)h * p.n_seqs + s) * p.T_max + t;
-    const float c = p.c_log2;
     const bool dense = p.lam_raw == INFINITY;
+    float c = p.c_log2;           // raw score -> base-2 exponent
+    float lam_raw = p.lam_raw;    // lambda in raw score units
+    float osc = 1.f;              // output scale
+    if constexpr (F8) {
+        const float sqk = p.q_scale[h] * p.k_scale[g];
+        c = p.c_log2 * sqk;
+        if (!dense) lam_raw = p.lam / (p.scale * sqk);
+        osc = p.v_scale[g];
+    }
 
-    const __bf16 *kg = (const __bf16 *)p.k + (int64_t)g * p.k_sh;
-    const __bf16 *vg = (const __bf16 *)p.v + (int64_t)g * p.v_sh;
+    const char *kg = (const char *)p.k + (int64_t)g * p.k_sh * ES;
+    const char *vg = (const char *)p.v + (int64_t)g * p.v_sh * ES;
+    const int64_t kstb = p.k_st * ES;  // bytes between tokens
+    const int64_t vstb = p.v_st * ES;
 
-    // Q^T fragments (MFMA B operand): lane holds Q[qrow][16ks + 8hh .. +7].
-    bf16x8 qf[KS];
+    // Q^T fragments (MFMA B operand). bf16: lane holds Q[qrow][16ks + 8hh .. +7];
+    // fp8: lane holds Q[qrow][64ks + 32hh .. +31]. The K operand reads below use
+    // the same dims per (lane half, byte), so the contraction pairs like with like.
+    typedef typename std::conditional<F8, i32x8, bf16x8>::type QFrag;
+    QFrag qf[KS];
     {
-        const __bf16 *qp = (const __bf16 *)p.q + (int64_t)(base + (valid ? qrow : 0)) * p.q_st +
-                           (int64_t)h * p.q_sh + 8 * hh;
+        const char *qp = (const char *)p.q + ((int64_t)(base + (valid ? qrow : 0)) * p.q_st + (int64_t)h * p.q_sh) * ES;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            bf16x8 x = *(const bf16x8 *)(qp + 16 * ks);
-            if (!valid) x = bf16x8{};
-            qf[ks] = x;
+            if constexpr (F8) {
+                const u32x4 lo = *(const u32x4 *)(qp + 64 * ks + 32 * hh);
+                const u32x4 hi = *(const u32x4 *)(qp + 64 * ks + 32 * hh + 16);
+                i32x8 x = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+                if (!valid) x = i32x8{};
+                qf[ks] = x;
+            } else {
+                bf16x8 x = *(const bf16x8 *)(qp + 2 * (16 * ks + 8 * hh));
+                if (!valid) x = bf16x8{};
+                qf[ks] = x;
+            }
         }
     }
 
     // Copy the key/value block starting at key kb into an LDS buffer. Wave w's
     // i-th copy fills the 1 KB segment i*NW + w; lane l writes physical chunk
-    // l % CPR of row segment*RPK + l / CPR and fetches the logical chunk that
-    // the swizzle maps there. Rows past the sequence end re-read its last row
-    // (finite data, always masked). For packed K/V the per-lane element offset
-    // inside a block is fixed, so it is computed once.
-    // Copy i covers rows crow0 + i*CSTEP. When CSTEP is a multiple of the swizzle period (16
-    // rows) the logical chunk is the same for every copy and the in-block element offset is
-    // crow0*stride + chunk + i*CSTEP*stride; otherwise the chunk is recomputed per copy.
-    constexpr int CSTEP = NW * RPK;
+    // l % KCPR of row segment*KRPK + l / KCPR and fetches the logical chunk that
+    // the swizzle maps there (fp8 V staging: no swizzle). Rows past the sequence
+    // end re-read its last row (finite data, always masked). Copy i covers rows
+    // crow0 + i*CSTEP; when CSTEP is a multiple of the swizzle period (16 rows)
+    // the fetched chunk is the same for every copy and, for packed K/V, the
+    // in-block byte offset is crow0*stride + chunk + i*CSTEP*stride.
+    auto kswz = [](int r) -> int {
+        if constexpr (F8) return chunk_swz8(r);
+        else return chunk_swz<D>(r);
+    };
+    constexpr int CSTEP = NW * KRPK;
     constexpr bool kFixedChunk = CSTEP % 16 == 0;
-    const int crow0 = w * RPK + lane / CPR;
-    const int lc8 = 8 * ((lane % CPR) ^ chunk_swz<D>(crow0));
-    const int kofs0 = (int)(crow0 * p.k_st) + lc8;
-    const int vofs0 = (int)(crow0 * p.v_st) + lc8;
-    auto copy_block = [&](const __bf16 *src, int64_t st, int ofs0, int kb, char *dst) {
+    const int crow0 = w * KRPK + lane / KCPR;
+    const int lcK = 16 * ((lane % KCPR) ^ kswz(crow0));
+    const int lcV = F8 ? 16 * (lane % KCPR) : lcK;
+    const int kofs0 = (int)(crow0 * kstb) + lcK;
+    const int vofs0 = (int)(crow0 * vstb) + lcV;
+    auto copy_block = [&](const char *src, int64_t stb, int ofs0, int kb, char *dst, bool swz) {
         if (!PAGED && kFixedChunk && kb + BK <= L) {
-            const __bf16 *blk = src + (int64_t)(base + kb) * st + ofs0;
+            const char *blk = src + (int64_t)(base + kb) * stb + ofs0;
 #pragma unroll
             for (int i = 0; i < CI; ++i)
-                lds_copy16(blk + (int64_t)(i * CSTEP) * st, dst + (i * NW + w) * 1024);
+                lds_copy16(blk + (int64_t)(i * CSTEP) * stb, dst + (i * NW + w) * 1024);
         } else {
 #pragma unroll
             for (int i = 0; i < CI; ++i) {
                 const int r = crow0 + i * CSTEP;
                 const int kk = min(kb + r, L - 1);
-                const int lci8 = kFixedChunk ? lc8 : 8 * ((lane % CPR) ^ chunk_swz<D>(r));
-                const __bf16 *gp = src + kv_row<PAGED>(p, s, base, kk, st) + lci8;
+                const int lci = !swz ? 16 * (lane % KCPR) : kFixedChunk ? lcK : 16 * ((lane % KCPR) ^ kswz(r));
+                const char *gp = src + kv_row<PAGED>(p, s, base, kk, stb) + lci;
                 lds_copy16(gp, dst + (i * NW + w) * 1024);
+            }
+        }
+    };
+    // fp8: widen this wave's own staged V bytes (its copies of the block, landed
+    // once vmcnt says so) into the bf16 V buffer, in the bf16 row swizzle.
+    auto widen_v = [&]() {
+        if constexpr (F8) {
+#pragma unroll
+            for (int i = 0; i < CI; ++i) {
+                const int r = crow0 + i * CSTEP;
+                const int c16 = lane % KCPR;
+                const u32x4 x = *(const u32x4 *)(sV8 + (i * NW + w) * 1024 + 16 * lane);
+                const u32x4 lo = {fp8x2_to_bf16x2<false>(x[0]), fp8x2_to_bf16x2<true>(x[0]),
+                                  fp8x2_to_bf16x2<false>(x[1]), fp8x2_to_bf16x2<true>(x[1])};
+                const u32x4 hi = {fp8x2_to_bf16x2<false>(x[2]), fp8x2_to_bf16x2<true>(x[2]),
+                                  fp8x2_to_bf16x2<false>(x[3]), fp8x2_to_bf16x2<true>(x[3])};
+                char *row = sV[0] + r * VROWB;
+                *(u32x4 *)(row + (((2 * c16) ^ chunk_swz<D>(r)) << 4)) = lo;
+                *(u32x4 *)(row + (((2 * c16 + 1) ^ chunk_swz<D>(r)) << 4)) = hi;
             }
         }
     };
@@ -291,8 +374,8 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, 1) fwd_bf16(FwdParams p) {
     SkipLog lg;
 
     // K operand reads: row 32mt + ln (the swizzle repeats every 16 rows, so it is that of row ln).
-    const int krow = ln * ROWB;
-    const int ksw = chunk_swz<D>(ln);
+    const int krow = ln * KROWB;
+    const int ksw = kswz(ln);
 
     // PV operand reads: contraction chunk cc = 2mt + u covers keys 32mt + 16u + 8(i'/4) + 4hh + i'%4
     // (i' = 0..7). Two transposing reads give lane (dim d, half hh) those 8 keys: in each 16-lane
@@ -310,7 +393,7 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, 1) fwd_bf16(FwdParams p) {
             for (int dt = 0; dt < DT; ++dt) {
                 const int d = 32 * dt + dsub;
                 const int r0 = 16 * u + 4 * (grp >> 1) + (gi >> 2);
-                vrd_off[u][dt] = r0 * ROWB + (((d >> 3) ^ chunk_swz<D>(r0)) << 4) + (d & 7) * 2;
+                vrd_off[u][dt] = r0 * VROWB + (((d >> 3) ^ chunk_swz<D>(r0)) << 4) + (d & 7) * 2;
             }
     }
 
@@ -320,8 +403,8 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, 1) fwd_bf16(FwdParams p) {
         for (int cc = 0; cc < PC; ++cc) {
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
-                const int o0 = vrd_off[cc & 1][dt] + (cc >> 1) * 32 * ROWB;
-                const int o8 = (D == 128 ? (o0 ^ 16) : o0) + 8 * ROWB;
+                const int o0 = vrd_off[cc & 1][dt] + (cc >> 1) * 32 * VROWB;
+                const int o8 = (D == 128 ? (o0 ^ 16) : o0) + 8 * VROWB;
                 const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(BSP_LDS(bf16x4, vbuf + o0));
                 const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(BSP_LDS(bf16x4, vbuf + o8));
                 const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -330,7 +413,7 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, 1) fwd_bf16(FwdParams p) {
         }
     };
 
-    copy_block(kg, p.k_st, kofs0, 0, sK[0]);
+    copy_block(kg, kstb, kofs0, 0, sK[0], true);
     wait_vmem_all();
     __syncthreads();
 
@@ -342,7 +425,7 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, 1) fwd_bf16(FwdParams p) {
         const int kb = j * BK;
         const int cur = j & 1;
         const bool has_next = j + 1 < nblk;
-        if (has_next) copy_block(kg, p.k_st, kofs0, kb + BK, sK[cur ^ 1]);
+        if (has_next) copy_block(kg, kstb, kofs0, kb + BK, sK[cur ^ 1], true);
 
         // ---- S^T = K Q^T : sacc[mt] holds keys 32mt + 8(i/4) + 4hh + i%4 for query qrow.
         // The k-step loop is outermost so that consecutive MFMAs use independent accumulators.
@@ -354,8 +437,17 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, 1) fwd_bf16(FwdParams p) {
         for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                const bf16x8 a = *(const bf16x8 *)(kbuf + krow + 32 * mt * ROWB + (((2 * ks + hh) ^ ksw) << 4));
-                sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sacc[mt], 0, 0, 0);
+                const char *rowp = kbuf + krow + 32 * mt * KROWB;
+                if constexpr (F8) {
+                    const u32x4 lo = *(const u32x4 *)(rowp + (((4 * ks + 2 * hh) ^ ksw) << 4));
+                    const u32x4 hi = *(const u32x4 *)(rowp + (((4 * ks + 2 * hh + 1) ^ ksw) << 4));
+                    const i32x8 a = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                     (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+                    sacc[mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf[ks], sacc[mt], 0, 0, 0, 0, 0, 0);
+                } else {
+                    const bf16x8 a = *(const bf16x8 *)(rowp + (((2 * ks + hh) ^ ksw) << 4));
+                    sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sacc[mt], 0, 0, 0);
+                }
             }
         }
         // ---- causal mask (only where the block reaches past this wave's first query)
@@ -376,7 +468,7 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, 1) fwd_bf16(FwdParams p) {
 
         // ---- skip decision: every valid row of the head's tile must have gap > lambda
         if (!dense) {
-            const bool ok = !valid || (mloc == -INFINITY) || (m_dec - mloc > p.lam_raw);
+            const bool ok = !valid || (mloc == -INFINITY) || (m_dec - mloc > lam_raw);
             const int wall = __all(ok);
             if (lane == 0) sVote[w] = wall;
         }
@@ -384,6 +476,7 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, 1) fwd_bf16(FwdParams p) {
         if (v_prev) {
             if (has_next) wait_vmem_leave<CI>();
             else wait_vmem_all();
+            widen_v();
         }
         __syncthreads();  // B1: votes and V_{j-1} visible; every wave is done with QK_j
         bool skip = false;
@@ -400,7 +493,10 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, 1) fwd_bf16(FwdParams p) {
             }
             if (wq == 0) log_decision(p, lg, bm_row, j, nblk, skip, lane == 0);
         }
-        if (any_keep) copy_block(vg, p.v_st, vofs0, kb, sV[cur]);
+        if (any_keep) {
+            if constexpr (F8) copy_block(vg, vstb, vofs0, kb, sV8, false);
+            else copy_block(vg, vstb, vofs0, kb, sV[cur], true);
+        }
 
         // ---- softmax of block j, overlapped with the pending PV of the previous kept block
         float alpha = 1.f;
@@ -420,7 +516,7 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, 1) fwd_bf16(FwdParams p) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) sacc[mt][i] = __builtin_amdgcn_exp2f(fmaf(sacc[mt][i], c, -mc));
         }
-        if (pend) pv_block(pprev, sV[cur ^ 1]);
+        if (pend) pv_block(pprev, sV[F8 ? 0 : (cur ^ 1)]);
         if (!skip) {
             float rs = 0.f;
 #pragma unroll
@@ -451,13 +547,14 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, 1) fwd_bf16(FwdParams p) {
     }
     if (v_prev) {
         wait_vmem_all();
+        widen_v();
         __syncthreads();
     }
-    if (pend) pv_block(pprev, sV[(nblk - 1) & 1]);
+    if (pend) pv_block(pprev, sV[F8 ? 0 : ((nblk - 1) & 1)]);
 
     // ---- epilogue: normalise, store O (bf16) and LSE (natural log)
     if (valid) {
-        const float inv = 1.f / l_run;
+        const float inv = osc / l_run;
         __bf16 *op = (__bf16 *)p.o + (int64_t)(base + qrow) * p.o_st + (int64_t)h * p.o_sh;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
@@ -475,7 +572,6 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, 1) fwd_bf16(FwdParams p) {
         if (p.visited_count) atomicAdd(&p.visited_count[h], (unsigned long long)nblk);
     }
 }
-
 // ---------------------------------------------------------------------------
 // fp32 kernel: QK^T and PV on v_mfma_f32_32x32x2_f32 (one element per lane
 // per operand, so V needs no transpose).
@@ -684,19 +780,26 @@ bsp_status_t check_tensor(const char *name, const bsp_tensor_t *x, int heads, in
 
 typedef void (*kernel_fn)(FwdParams);
 
+template <int IN, int D, int BQ, int BK>
+kernel_fn pick_mfma(bool paged, int hpw) {
+    if (hpw == 2) return paged ? fwd_mfma<IN, D, BQ, BK, true, 2> : fwd_mfma<IN, D, BQ, BK, false, 2>;
+    return paged ? fwd_mfma<IN, D, BQ, BK, true, 1> : fwd_mfma<IN, D, BQ, BK, false, 1>;
+}
+
 template <int D, int BQ, int BK>
 kernel_fn pick_kernel(int dtype, bool paged, int hpw) {
-    if (dtype == BSP_BF16) {
-        if (hpw == 2) return paged ? fwd_bf16<D, BQ, BK, true, 2> : fwd_bf16<D, BQ, BK, false, 2>;
-        return paged ? fwd_bf16<D, BQ, BK, true, 1> : fwd_bf16<D, BQ, BK, false, 1>;
+    if (dtype == BSP_BF16) return pick_mfma<BSP_BF16, D, BQ, BK>(paged, hpw);
+    if (dtype == BSP_FP8_E4M3) {
+        if constexpr (D == 128) return pick_mfma<BSP_FP8_E4M3, D, BQ, BK>(paged, hpw);
+        return nullptr;  // fp8 kernels are built for head_dim 128 only
     }
     if (dtype == BSP_F32) return paged ? fwd_f32<D, BQ, BK, true> : fwd_f32<D, BQ, BK, false>;
     return nullptr;
 }
 
-// Query heads per workgroup: bf16 kernels pair the query heads of a KV head
-// when the group size is even.
-int heads_per_workgroup(int dtype, int group) { return (dtype == BSP_BF16 && group % 2 == 0) ? 2 : 1; }
+// Query heads per workgroup: the bf16 and fp8 kernels pair the query heads of
+// a KV head when the group size is even.
+int heads_per_workgroup(int dtype, int group) { return (dtype != BSP_F32 && group % 2 == 0) ? 2 : 1; }
 
 kernel_fn find_kernel(int dtype, int D, int BQ, int BK, bool paged, int hpw) {
 #define BSP_CASE(d, bq, bk) \
@@ -869,6 +972,11 @@ bsp_status_t bsp_attn_fwd(const bsp_tensor_t *q, const bsp_tensor_t *k, const bs
         const double scale = 1.0 / sqrt((double)head_dim);
         p.c_log2 = (float)(scale * 1.4426950408889634);
         p.lam_raw = isinf(lambda) ? INFINITY : (float)((double)lambda / scale);
+        p.q_scale = q->scale;
+        p.k_scale = k->scale;
+        p.v_scale = v->scale;
+        p.scale = (float)scale;
+        p.lam = lambda;
         hipLaunchKernelGGL(fn, dim3((unsigned)grid64), dim3(block_q * 2 * hpw), 0, hs, p);
     }
     const hipError_t e = hipGetLastError();

@@ -121,6 +121,10 @@ typedef struct {
  * block_table: paged-cache descriptor or NULL.
  * n_heads_q % n_heads_kv == 0; query head h reads KV head h / (n_heads_q / n_heads_kv).
  * head_dim in {64, 128}; (block_q, block_k) in {(64,64), (128,64), (128,128)}.
+ *   FP8_E4M3 inputs: head_dim 128 only (other head_dim: BSP_ERR_UNSUPPORTED);
+ *   the q, k and v descriptors must all carry scales (positive, finite), read
+ *   on the device as float[n_heads_q] for q and float[n_heads_kv] for k and v.
+ *   QK^T runs on fp8 MFMA; P and V (widened exactly) enter PV as bf16.
  * lambda >= 0 or +inf (NaN and negative values are rejected).
  * skip_mask_out: observability outputs or NULL.
  * stream: hipStream_t (as void*), NULL for the default stream.

@@ -5,8 +5,13 @@ For one (inputs, block sizes, lambda) case:
   2. run the oracle on the same inputs for a set of work items (all, or a
      deterministic sample for large workloads);
   3. the skip bitmaps must be identical on every visited pair whose decision
-     margin |min gap - lambda| exceeds 1e-3 (scores are fp32 on the GPU and
-     fp64 in the oracle, so pairs inside that band may legitimately flip);
+     margin |min gap - lambda| exceeds the band: 1e-3 for fp32 and bf16
+     inputs (scores are fp32 on the GPU and fp64 in the oracle, so pairs
+     inside that band may legitimately flip) and 1e-2 for fp8 inputs, whose
+     MFMA dot product is not rounded once at the end: measured on gfx950, it
+     drops low-order bits of the smaller products, an error up to ~3e-5 of
+     sum_i |q_i k_i|, i.e. up to ~3e-3 per score (~6.5e-3 per gap) on the
+     128K fp8 workload, where the scaled sum_i |q_i k_i| reaches ~107;
   4. where they differ inside the band, the oracle is re-run with the GPU's
      decisions forced, and outputs are compared against that run;
   5. O must satisfy the dtype's tolerance (bf16: max-abs <= 2e-2 and
@@ -27,7 +32,7 @@ import numpy as np
 import oracle
 import synth
 
-MARGIN_BAND = 1e-3
+MARGIN_BAND = {"f32": 1e-3, "bf16": 1e-3, "fp8": 1e-2}
 TOL = {
     "f32": dict(max_abs=1e-4, mean_abs=1e-4, lse=1e-4),
     "bf16": dict(max_abs=2e-2, mean_abs=2e-3, lse=1e-2),
@@ -111,7 +116,7 @@ def compare(inp: synth.Inputs, gpu: Dict, block_q: int, block_k: int, lam: float
     diff = (gbits != ref.skip) & vis
     if diff.any():
         margin = np.abs(ref.mingap - lam)
-        hard = diff & ~(margin <= MARGIN_BAND)
+        hard = diff & ~(margin <= MARGIN_BAND[inp.dtype])
         if hard.any():
             idx = np.argwhere(hard)[:5]
             rep.problems.append(f"{int(hard.sum())} skip decisions differ outside the margin band, e.g. "

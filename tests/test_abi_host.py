@@ -163,6 +163,13 @@ def test_fp8_requires_scales(lib):
     assert st == bsp.BSP_ERR_INVALID_ARG
 
 
+def test_fp8_head_dim_64_is_unsupported(lib):
+    D = 64
+    t = lambda H: Tensor(FAKE, bsp.BSP_FP8_E4M3, H * D, D, FAKE)
+    st = _call(head_dim=D, q=t(32), k=t(8), v=t(8), o=Tensor(FAKE, bsp.BSP_BF16, 32 * D, D, None))
+    assert st == bsp.BSP_ERR_UNSUPPORTED, bsp.last_error_detail()
+
+
 def test_binding_fails_loudly_without_library(tmp_path):
     import importlib
 

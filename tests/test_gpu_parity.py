@@ -57,6 +57,24 @@ def test_small_cases(dtype, inst, paged):
     assert reps[2].n_skipped > 0
 
 
+FP8_INSTANCES = [(128, 64, 64), (128, 128, 64), (128, 128, 128)]
+
+
+@pytest.mark.parametrize("inst", FP8_INSTANCES, ids=lambda x: "d%d_q%d_k%d" % x)
+@pytest.mark.parametrize("paged", [False, True], ids=["packed", "paged"])
+@pytest.mark.parametrize("gqa", [(4, 2), (3, 1)], ids=["g2", "g3"])
+def test_small_cases_fp8(inst, paged, gqa):
+    D, bq, bk = inst
+    Hq, Hkv = gqa
+    seqlens = (300, 0, 129, 1, 64)
+    inp = synth.build_inputs(seqlens, Hq, Hkv, D, "fp8", rho=0.95, n_vert=2, code=209, paged=paged, page_size=64,
+                             sink_gain=6.0)
+    _log(f"small case fp8 D={D} bq={bq} bk={bk} paged={paged} Hq={Hq} Hkv={Hkv}")
+    reps = parity.check_case(inp, bq, bk, [math.inf, 2.0, 0.0], paged=paged)
+    assert reps[0].n_skipped == 0
+    assert reps[2].n_skipped > 0
+
+
 def test_xcd_mapping_with_eight_kv_heads():
     # 8 KV heads switch on the XCD-partitioned work order
     inp = synth.build_inputs((517, 130), 16, 8, 128, "bf16", rho=0.97, n_vert=4, code=202)
@@ -100,6 +118,14 @@ def test_llama8b_32k_bf16_sampled():
 
 def test_varlen16_paged_bf16_sampled():
     _sampled("varlen16_paged_bf16", heads=[5, 30], tile_stride=37)
+
+
+def test_llama8b_128k_bf16_sampled():
+    _sampled("llama8b_128k", heads=[0, 21], tile_stride=211, dtype="bf16")
+
+
+def test_llama8b_128k_fp8_sampled():
+    _sampled("llama8b_128k", heads=[0, 21], tile_stride=211, dtype="fp8")
 
 
 def test_repeat_runs_are_bit_identical():
