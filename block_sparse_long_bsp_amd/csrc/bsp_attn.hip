@@ -122,13 +122,20 @@ __device__ __forceinline__ int64_t kv_row(const FwdParams &p, int s, int base, i
     }
 }
 
-__device__ __forceinline__ float wave_max16(const f32x16 &a) {
-    float m = fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3]));
-    m = fmaxf(m, fmaxf(fmaxf(a[4], a[5]), fmaxf(a[6], a[7])));
-    m = fmaxf(m, fmaxf(fmaxf(a[8], a[9]), fmaxf(a[10], a[11])));
-    m = fmaxf(m, fmaxf(fmaxf(a[12], a[13]), fmaxf(a[14], a[15])));
+// Maximum of the 16 values with m folded in, as a chain of three-operand
+// maxima (v_max3_f32; the device code is built without NaN operands, so the
+// compiler needs no operand canonicalisation).
+__device__ __forceinline__ float max_fold16(float m, const f32x16 &a) {
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) m = fmaxf(fmaxf(m, a[i]), a[i + 1]);
     return m;
 }
+__device__ __forceinline__ float wave_max16(const f32x16 &a) { return max_fold16(-INFINITY, a); }
+
+// Keeps the scheduler from moving any instruction across this point: the
+// interleaving written in the source (matrix, vector and copy instructions of
+// independent work) is kept at that granularity.
+#define SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
 
 // Shared epilogue of the decision: record the bit and the count.
 struct SkipLog {
@@ -169,16 +176,20 @@ __device__ __forceinline__ void log_decision(const FwdParams &p, SkipLog &lg, in
 // dim) are free of bank conflicts.
 //
 // Per key block j (software-pipelined: the PV product of a kept block runs one
-// block later, interleaved with the next block's softmax):
-//   1. start the copy of K_{j+1} into the other K buffer;
-//   2. S^T = K_j Q^T; causal mask on the diagonal block; row maxima; per-head
-//      vote; (fp8: widen the staged V_{j-1} into the bf16 V buffer); barrier
-//      B1 (which also publishes V_{j-1});
-//   3. start the copy of V_j (bf16: into its buffer; fp8: into the staging
-//      buffer) only if some head keeps block j (with lambda = +inf every block
-//      is kept and there is no vote);
-//   4. softmax of block j (if kept) while O^T += V^T P^T of the previous kept
-//      block runs from the V buffer; barrier B2 publishes K_{j+1}.
+// block later, next to the following block's softmax):
+//   1. S^T = K_j Q^T, with the copy instructions of K_{j+1} spread over its
+//      MFMAs; causal mask on the diagonal block; row maxima; per-head vote;
+//      (fp8: widen the staged V_{j-1} into the bf16 V buffer); barrier B1
+//      (which also publishes V_{j-1});
+//   2. start the copy of V_j (bf16: into its buffer; fp8: into the staging
+//      buffer) only if some head keeps block j;
+//   3. softmax of block j (if kept) and O^T += V^T P^T of the previous kept
+//      block from the V buffer; barrier B2 publishes K_{j+1}.
+// Dense mode (lambda = +inf) is a kernel of its own: every block is kept, there
+// is no vote, and step 3 interleaves each PV MFMA with a share of the
+// exponentials and the row sum (fixed by scheduling fences), so that matrix
+// cores and vector ALU overlap. The sparse kernel keeps step 3 unfused: the
+// skip branches and the fused order together do not fit in the registers.
 // The exponent reference max moves only when the running max has grown by
 // more than 2^8 (base-2 units), so the O/l rescale is rare; the running max
 // used by the skip decision is tracked exactly and separately.
@@ -213,6 +224,12 @@ __device__ __forceinline__ void lds_copy16(const void *gptr, const void *lds) {
     const uint32_t la = (uint32_t)(uintptr_t)BSP_LDS(const void, lds);
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(la) : "m0");
 }
+// Same copy with a wave-uniform 64-bit base (SGPR pair) and a per-lane 32-bit
+// byte offset: the per-copy address arithmetic stays on the scalar unit.
+__device__ __forceinline__ void lds_copy16_sb(const void *sbase, uint32_t voff, const void *lds) {
+    const uint32_t la = (uint32_t)(uintptr_t)BSP_LDS(const void, lds);
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(la) : "m0");
+}
 template <int N>
 __device__ __forceinline__ void wait_vmem_leave() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 
@@ -224,7 +241,7 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t x) {
     return __builtin_bit_cast(uint32_t, y);
 }
 
-template <int IN, int D, int BQ, int BK, bool PAGED, int HPW>
+template <int IN, int D, int BQ, int BK, bool PAGED, int HPW, bool DENSE>
 __global__ void __launch_bounds__(BQ * 2 * HPW, 1) fwd_mfma(FwdParams p) {
     constexpr bool F8 = IN == BSP_FP8_E4M3;
     constexpr int WPH = BQ / 32;     // waves per head
@@ -270,7 +287,7 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, 1) fwd_mfma(FwdParams p) {
     const int qrow = q0 + ln;
     const bool valid = qrow < L;
     const int64_t bm_row = ((int64_t)h * p.n_seqs + s) * p.T_max + t;
-    const bool dense = p.lam_raw == INFINITY;
+    constexpr bool dense = DENSE;  // lambda = +inf: every block is kept, no vote
     float c = p.c_log2;           // raw score -> base-2 exponent
     float lam_raw = p.lam_raw;    // lambda in raw score units
     float osc = 1.f;              // output scale
@@ -309,14 +326,18 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, 1) fwd_mfma(FwdParams p) {
         }
     }
 
-    // Copy the key/value block starting at key kb into an LDS buffer. Wave w's
-    // i-th copy fills the 1 KB segment i*NW + w; lane l writes physical chunk
-    // l % KCPR of row segment*KRPK + l / KCPR and fetches the logical chunk that
-    // the swizzle maps there (fp8 V staging: no swizzle). Rows past the sequence
-    // end re-read its last row (finite data, always masked). Copy i covers rows
-    // crow0 + i*CSTEP; when CSTEP is a multiple of the swizzle period (16 rows)
-    // the fetched chunk is the same for every copy and, for packed K/V, the
-    // in-block byte offset is crow0*stride + chunk + i*CSTEP*stride.
+    // Copy of the key/value block starting at key kb into an LDS buffer. Wave
+    // w's i-th copy instruction fills the 1 KB segment i*NW + w; lane l writes
+    // physical chunk l % KCPR of row crow0 + i*CSTEP and fetches the logical
+    // chunk that the swizzle maps there (fp8 V staging: no swizzle). When CSTEP
+    // is a multiple of the swizzle period (16 rows) that chunk is the same for
+    // every copy of the lane. Rows past the sequence end re-read its last row
+    // (finite data, always masked; the K copy one block past the last one of a
+    // tile is of this kind). Each copy instruction is issued on its own, so
+    // that the copies of a block can be spread over the matrix work. The code is
+    // branch-free: packed K/V use a wave-uniform base at row kb0 = min(kb, L-1)
+    // and a per-lane 32-bit offset (kk - kb0) * stride + chunk, which lies in
+    // [0, (BK - 1) * stride + 16 * (KCPR - 1)] because kb0 <= kk <= L - 1.
     auto kswz = [](int r) -> int {
         if constexpr (F8) return chunk_swz8(r);
         else return chunk_swz<D>(r);
@@ -325,25 +346,21 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, 1) fwd_mfma(FwdParams p) {
     constexpr bool kFixedChunk = CSTEP % 16 == 0;
     const int crow0 = w * KRPK + lane / KCPR;
     const int lcK = 16 * ((lane % KCPR) ^ kswz(crow0));
-    const int lcV = F8 ? 16 * (lane % KCPR) : lcK;
-    const int kofs0 = (int)(crow0 * kstb) + lcK;
-    const int vofs0 = (int)(crow0 * vstb) + lcV;
-    auto copy_block = [&](const char *src, int64_t stb, int ofs0, int kb, char *dst, bool swz) {
-        if (!PAGED && kFixedChunk && kb + BK <= L) {
-            const char *blk = src + (int64_t)(base + kb) * stb + ofs0;
-#pragma unroll
-            for (int i = 0; i < CI; ++i)
-                lds_copy16(blk + (int64_t)(i * CSTEP) * stb, dst + (i * NW + w) * 1024);
+    auto copy_one = [&](const char *src, int64_t stb, int kb, char *dst, bool swz, int i) {
+        const int r = crow0 + i * CSTEP;
+        const int kk = min(kb + r, L - 1);
+        const int lci = !swz ? 16 * (lane % KCPR) : kFixedChunk ? lcK : 16 * ((lane % KCPR) ^ kswz(r));
+        if constexpr (PAGED) {
+            lds_copy16(src + kv_row<PAGED>(p, s, base, kk, stb) + lci, dst + (i * NW + w) * 1024);
         } else {
-#pragma unroll
-            for (int i = 0; i < CI; ++i) {
-                const int r = crow0 + i * CSTEP;
-                const int kk = min(kb + r, L - 1);
-                const int lci = !swz ? 16 * (lane % KCPR) : kFixedChunk ? lcK : 16 * ((lane % KCPR) ^ kswz(r));
-                const char *gp = src + kv_row<PAGED>(p, s, base, kk, stb) + lci;
-                lds_copy16(gp, dst + (i * NW + w) * 1024);
-            }
+            const int kb0 = min(kb, L - 1);
+            lds_copy16_sb(src + (int64_t)(base + kb0) * stb, (uint32_t)((kk - kb0) * stb) + (uint32_t)lci,
+                          dst + (i * NW + w) * 1024);
         }
+    };
+    auto copy_block = [&](const char *src, int64_t stb, int kb, char *dst, bool swz) {
+#pragma unroll
+        for (int i = 0; i < CI; ++i) copy_one(src, stb, kb, dst, swz, i);
     };
     // fp8: widen this wave's own staged V bytes (its copies of the block, landed
     // once vmcnt says so) into the bf16 V buffer, in the bf16 row swizzle.
@@ -380,78 +397,94 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, 1) fwd_mfma(FwdParams p) {
     // PV operand reads: contraction chunk cc = 2mt + u covers keys 32mt + 16u + 8(i'/4) + 4hh + i'%4
     // (i' = 0..7). Two transposing reads give lane (dim d, half hh) those 8 keys: in each 16-lane
     // group, source lane i points at key 32mt + 16u + 4hh + i/4 (+8), dims d0 + 4(i%4)..+3. The
-    // swizzle depends on the key only through key % 16, which is the same for every mt.
-    // The second read (keys +8) differs only in the swizzle bit (D = 128) or not at all (D = 64).
-    int vrd_off[2][DT];
+    // swizzle depends on the key only through key % 16, so the offset of chunk cc is that of
+    // chunk 0 plus the immediate cc * 16 * VROWB; the second read (keys +8) differs only in the
+    // swizzle bit (D = 128) or not at all (D = 64).
+    int vrd_off[DT];
     {
         const int grp = lane >> 4;
         const int gi = lane & 15;
         const int dsub = 16 * (grp & 1) + 4 * (gi & 3);
+        const int r0 = 4 * (grp >> 1) + (gi >> 2);
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                const int d = 32 * dt + dsub;
-                const int r0 = 16 * u + 4 * (grp >> 1) + (gi >> 2);
-                vrd_off[u][dt] = r0 * VROWB + (((d >> 3) ^ chunk_swz<D>(r0)) << 4) + (d & 7) * 2;
-            }
+        for (int dt = 0; dt < DT; ++dt) {
+            const int d = 32 * dt + dsub;
+            vrd_off[dt] = r0 * VROWB + (((d >> 3) ^ chunk_swz<D>(r0)) << 4) + (d & 7) * 2;
+        }
     }
+    auto vread_at = [&](const char *vbuf, int cc, int dt) -> bf16x8 {
+        const int o0 = vrd_off[dt] + cc * 16 * VROWB;
+        const int o8 = (D == 128 ? (vrd_off[dt] ^ 16) : vrd_off[dt]) + cc * 16 * VROWB + 8 * VROWB;
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(BSP_LDS(bf16x4, vbuf + o0));
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(BSP_LDS(bf16x4, vbuf + o8));
+        return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
 
     // O^T += V^T P^T for a kept block whose bf16 probabilities are in pp and whose V is in vbuf.
     auto pv_block = [&](const bf16x8 *pp, const char *vbuf) {
 #pragma unroll
         for (int cc = 0; cc < PC; ++cc) {
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                const int o0 = vrd_off[cc & 1][dt] + (cc >> 1) * 32 * VROWB;
-                const int o8 = (D == 128 ? (o0 ^ 16) : o0) + 8 * VROWB;
-                const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(BSP_LDS(bf16x4, vbuf + o0));
-                const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(BSP_LDS(bf16x4, vbuf + o8));
-                const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pp[cc], oacc[dt], 0, 0, 0);
-            }
+            for (int dt = 0; dt < DT; ++dt)
+                oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vread_at(vbuf, cc, dt), pp[cc], oacc[dt], 0, 0, 0);
         }
     };
 
-    copy_block(kg, kstb, kofs0, 0, sK[0], true);
+    copy_block(kg, kstb, 0, sK[0], true);
     wait_vmem_all();
     __syncthreads();
 
     bf16x8 pprev[PC];       // probabilities of this wave's last kept block, PV still pending
     bool pend = false;      // wave-uniform: a PV is pending
     bool v_prev = false;    // workgroup-uniform: V of block j-1 was copied
+    constexpr int NE = 16 * MT;        // scores per lane per block
+    constexpr int NPV = PC * DT;       // MFMAs of the PV product
+    constexpr int EPG = NE / NPV;      // exponentials per PV MFMA
+    static_assert(NE % NPV == 0, "softmax/PV interleave must be even");
+    f32x16 sacc[MT];
+    float pe[NE];           // probabilities of the current block, element e = 16 mt + i
 
-    for (int j = 0; j < nblk; ++j) {
+    // ---- S^T = K_j Q^T : sacc[mt] holds keys 32mt + 8(i/4) + 4hh + i%4 for query qrow;
+    // causal mask; returns the row maximum over the block. MFMA f = ks*MT + mt
+    // (k-step outermost, so consecutive MFMAs use independent accumulators); its K
+    // operand is read one MFMA ahead, and the copy instructions of K_{j+1} are
+    // spread over the MFMAs (one every QSTEP), which keeps them from queueing at
+    // the memory unit all at once.
+    auto qk_phase = [&](int j) -> float {
         const int kb = j * BK;
-        const int cur = j & 1;
-        const bool has_next = j + 1 < nblk;
-        if (has_next) copy_block(kg, kstb, kofs0, kb + BK, sK[cur ^ 1], true);
-
-        // ---- S^T = K Q^T : sacc[mt] holds keys 32mt + 8(i/4) + 4hh + i%4 for query qrow.
-        // The k-step loop is outermost so that consecutive MFMAs use independent accumulators.
-        const char *kbuf = sK[cur];
-        f32x16 sacc[MT];
+        const char *kbuf = sK[j & 1];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) sacc[mt] = f32x16{};
+        constexpr int NQK = KS * MT;
+        constexpr int QSTEP = NQK / CI;
+        static_assert(NQK % CI == 0, "K copies must spread evenly over the QK MFMAs");
+        typedef typename std::conditional<F8, i32x8, bf16x8>::type KOp;
+        auto kread = [&](int f) -> KOp {
+            const int ks = f / MT, mt = f % MT;
+            const char *rowp = kbuf + krow + 32 * mt * KROWB;
+            if constexpr (F8) {
+                const u32x4 lo = *(const u32x4 *)(rowp + (((4 * ks + 2 * hh) ^ ksw) << 4));
+                const u32x4 hi = *(const u32x4 *)(rowp + (((4 * ks + 2 * hh + 1) ^ ksw) << 4));
+                return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+            } else {
+                return *(const bf16x8 *)(rowp + (((2 * ks + hh) ^ ksw) << 4));
+            }
+        };
+        KOp kop[NQK];
+        kop[0] = kread(0);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                const char *rowp = kbuf + krow + 32 * mt * KROWB;
-                if constexpr (F8) {
-                    const u32x4 lo = *(const u32x4 *)(rowp + (((4 * ks + 2 * hh) ^ ksw) << 4));
-                    const u32x4 hi = *(const u32x4 *)(rowp + (((4 * ks + 2 * hh + 1) ^ ksw) << 4));
-                    const i32x8 a = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                                     (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-                    sacc[mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf[ks], sacc[mt], 0, 0, 0, 0, 0, 0);
-                } else {
-                    const bf16x8 a = *(const bf16x8 *)(rowp + (((2 * ks + hh) ^ ksw) << 4));
-                    sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sacc[mt], 0, 0, 0);
-                }
+        for (int f = 0; f < NQK; ++f) {
+            if (f + 1 < NQK) kop[f + 1] = kread(f + 1);
+            const int ks = f / MT, mt = f % MT;
+            if constexpr (F8) sacc[mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kop[f], qf[ks], sacc[mt], 0, 0, 0, 0, 0, 0);
+            else sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[f], qf[ks], sacc[mt], 0, 0, 0);
+            if (f % QSTEP == 0) {  // K_{j+1} (rows clamped: past the last block it re-reads the end)
+                SCHED_FENCE();
+                copy_one(kg, kstb, kb + BK, sK[(j + 1) & 1], true, f / QSTEP);
+                SCHED_FENCE();
             }
         }
-        // ---- causal mask (only where the block reaches past this wave's first query)
-        if (kb + BK - 1 > q0) {
+        if (kb + BK - 1 > q0) {  // causal mask (only where the block reaches past this wave's first query)
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -460,29 +493,150 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, 1) fwd_mfma(FwdParams p) {
                     if (key > qrow) sacc[mt][i] = -INFINITY;
                 }
         }
-        // ---- local max of each row over the block
-        float mloc = wave_max16(sacc[0]);
+        float m = -INFINITY;
 #pragma unroll
-        for (int mt = 1; mt < MT; ++mt) mloc = fmaxf(mloc, wave_max16(sacc[mt]));
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+        for (int mt = 0; mt < MT; ++mt) m = max_fold16(m, sacc[mt]);
+        return fmaxf(m, __shfl_xor(m, 32));
+    };
 
-        // ---- skip decision: every valid row of the head's tile must have gap > lambda
-        if (!dense) {
-            const bool ok = !valid || (mloc == -INFINITY) || (m_dec - mloc > lam_raw);
-            const int wall = __all(ok);
-            if (lane == 0) sVote[w] = wall;
+    // Running max, lazy reference update; returns (in mc) the reference in
+    // base-2 units, and the rescale factor for O and l (resc: needed by a lane).
+    auto new_reference = [&](float mloc, float &alpha, bool &resc) -> float {
+        const float m_new = fmaxf(m_dec, mloc);
+        m_dec = m_new;
+        const bool need = (m_new - m_ref) * c > kRescaleLog2;  // also true while m_ref = -inf
+        resc = __any(need);
+        alpha = 1.f;
+        if (need) {
+            alpha = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_ref - m_new) * c);
+            m_ref = m_new;
         }
-        // V_{j-1} (copied during the previous block) must be in LDS before B1; K_{j+1} may still fly.
-        if (v_prev) {
-            if (has_next) wait_vmem_leave<CI>();
-            else wait_vmem_all();
+        return m_ref * c;
+    };
+    // O and l to the new reference (after the pending PV), l += row sum, and the
+    // bf16 probabilities of this block for its PV product.
+    auto finish_block = [&](float rs, float alpha, bool resc) {
+        rs += __shfl_xor(rs, 32);
+        if (resc) {
+            l_run *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+        }
+        l_run += rs;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) pprev[2 * mt + u][i] = (__bf16)pe[16 * mt + 8 * u + i];
+    };
+    auto exp_sum = [&](float mc) -> float {
+        float rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+        for (int e = 0; e < NE; ++e) pe[e] = __builtin_amdgcn_exp2f(fmaf(sacc[e >> 4][e & 15], c, -mc));
+#pragma unroll
+        for (int e = 0; e < NE; e += 2) {
+            rs0 += pe[e];
+            rs1 += pe[e + 1];
+        }
+        return rs0 + rs1;
+    };
+
+    // PV of the previous kept block (V in vbuf) interleaved with the exponentials
+    // and row sum of the current block: group g is PV MFMA g (V operand read one
+    // MFMA ahead) followed by the exponentials of elements EPG*g .. EPG*g + EPG - 1
+    // and the row sum of the previous group's elements, so the matrix cores and
+    // the vector ALU work side by side. The fences keep this order. Returns the
+    // row sum (this lane's half).
+    auto fused_pv_exp = [&](const char *vbuf, float mc) -> float {
+        auto vread = [&](int g) -> bf16x8 { return vread_at(vbuf, g / DT, g % DT); };
+        float rs0 = 0.f, rs1 = 0.f;
+        bf16x8 vop[NPV];
+        vop[0] = vread(0);
+#pragma unroll
+        for (int g = 0; g < NPV; ++g) {
+            if (g + 1 < NPV) vop[g + 1] = vread(g + 1);
+            oacc[g % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[g], pprev[g / DT], oacc[g % DT], 0, 0, 0);
+#pragma unroll
+            for (int e = EPG * g; e < EPG * (g + 1); ++e)
+                pe[e] = __builtin_amdgcn_exp2f(fmaf(sacc[e >> 4][e & 15], c, -mc));
+            if (g > 0) {
+#pragma unroll
+                for (int e = EPG * (g - 1); e < EPG * g; e += 2) {
+                    rs0 += pe[e];
+                    rs1 += pe[e + 1];
+                }
+            }
+            SCHED_FENCE();
+        }
+#pragma unroll
+        for (int e = NE - EPG; e < NE; e += 2) {
+            rs0 += pe[e];
+            rs1 += pe[e + 1];
+        }
+        return rs0 + rs1;
+    };
+
+    if constexpr (DENSE) {
+        // ---- dense mode: every block is kept. Block 0 has no pending PV; every
+        // later block runs the PV product of the previous block interleaved with
+        // its own exponentials and row sum: group g is PV MFMA g (V operand read
+        // two MFMAs ahead) followed by the exponentials of elements EPG*g ..
+        // EPG*g + EPG - 1 and the row sum of the previous group's elements, so the
+        // matrix cores and the vector ALU work side by side. The fences keep this
+        // order; the loop body has no branches, so the compiler keeps one register
+        // assignment for the accumulators.
+        {
+            const float mloc = qk_phase(0);
+            __syncthreads();  // B1: every wave is done with QK_0
+            if constexpr (F8) copy_block(vg, vstb, 0, sV8, false);
+            else copy_block(vg, vstb, 0, sV[0], true);
+            float alpha;
+            bool resc;
+            const float mc = new_reference(mloc, alpha, resc);
+            finish_block(exp_sum(mc), alpha, resc);
+            wait_vmem_leave<CI>();
+            __syncthreads();  // B2: K_1 in LDS
+        }
+        for (int j = 1; j < nblk; ++j) {
+            const int cur = j & 1;
+            const float mloc = qk_phase(j);
+            // V_{j-1} must be in LDS before B1; K_{j+1} may still fly.
+            wait_vmem_leave<CI>();
             widen_v();
+            __syncthreads();  // B1
+            if constexpr (F8) copy_block(vg, vstb, j * BK, sV8, false);
+            else copy_block(vg, vstb, j * BK, sV[cur], true);
+            float alpha;
+            bool resc;
+            const float mc = new_reference(mloc, alpha, resc);
+            finish_block(fused_pv_exp(sV[F8 ? 0 : (cur ^ 1)], mc), alpha, resc);
+            // B2: K_{j+1} is in LDS (loads complete in issue order; V_j, issued last, may still fly).
+            wait_vmem_leave<CI>();
+            __syncthreads();
         }
-        __syncthreads();  // B1: votes and V_{j-1} visible; every wave is done with QK_j
-        bool skip = false;
-        bool any_keep = true;
-        if (!dense) {
-            any_keep = false;
+        pend = true;
+        v_prev = true;
+    } else {
+        // ---- sparse mode: per block, the tile-wide vote decides skip or keep.
+        for (int j = 0; j < nblk; ++j) {
+            const int kb = j * BK;
+            const int cur = j & 1;
+            const float mloc = qk_phase(j);
+            // skip decision: every valid row of the head's tile must have gap > lambda
+            {
+                const bool ok = !valid || (mloc == -INFINITY) || (m_dec - mloc > lam_raw);
+                const int wall = __all(ok);
+                if (lane == 0) sVote[w] = wall;
+            }
+            // V_{j-1} (copied during the previous block) must be in LDS before B1; K_{j+1} may still fly.
+            if (v_prev) {
+                wait_vmem_leave<CI>();
+                widen_v();
+            }
+            __syncthreads();  // B1: votes and V_{j-1} visible; every wave is done with QK_j
+            bool skip = false;
+            bool any_keep = false;
 #pragma unroll
             for (int x = 0; x < HPW; ++x) {
                 bool sk = true;
@@ -492,61 +646,55 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, 1) fwd_mfma(FwdParams p) {
                 any_keep = any_keep || !sk;
             }
             if (wq == 0) log_decision(p, lg, bm_row, j, nblk, skip, lane == 0);
-        }
-        if (any_keep) {
-            if constexpr (F8) copy_block(vg, vstb, vofs0, kb, sV8, false);
-            else copy_block(vg, vstb, vofs0, kb, sV[cur], true);
-        }
-
-        // ---- softmax of block j, overlapped with the pending PV of the previous kept block
-        float alpha = 1.f;
-        bool resc = false;
-        if (!skip) {
-            const float m_new = fmaxf(m_dec, mloc);
-            m_dec = m_new;
-            const bool need = (m_new - m_ref) * c > kRescaleLog2;  // also true while m_ref = -inf
-            resc = __any(need);
-            if (need) {
-                alpha = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_ref - m_new) * c);
-                m_ref = m_new;
+            if (any_keep) {
+                if constexpr (F8) copy_block(vg, vstb, kb, sV8, false);
+                else copy_block(vg, vstb, kb, sV[cur], true);
             }
-            const float mc = m_ref * c;
+            // softmax of block j, then the pending PV of the previous kept block
+            // exponentials in place, then the pending PV, then row sum, rescale and
+            // the bf16 probabilities (the fused order of the dense loop does not fit
+            // the registers next to the skip branches)
+            float alpha = 1.f;
+            bool resc = false;
+            if (!skip) {
+                const float mc = new_reference(mloc, alpha, resc);
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
+                for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) sacc[mt][i] = __builtin_amdgcn_exp2f(fmaf(sacc[mt][i], c, -mc));
-        }
-        if (pend) pv_block(pprev, sV[F8 ? 0 : (cur ^ 1)]);
-        if (!skip) {
-            float rs = 0.f;
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) rs += sacc[mt][i];
-            rs += __shfl_xor(rs, 32);
-            if (resc) {  // after the pending PV: O and l are then both relative to the new reference
-                l_run *= alpha;
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+                    for (int i = 0; i < 16; ++i) sacc[mt][i] = __builtin_amdgcn_exp2f(fmaf(sacc[mt][i], c, -mc));
             }
-            l_run += rs;
+            if (pend) pv_block(pprev, sV[F8 ? 0 : (cur ^ 1)]);
+            if (!skip) {
+                float rs = 0.f;
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
+                for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                for (int u = 0; u < 2; ++u)
+                    for (int i = 0; i < 16; ++i) rs += sacc[mt][i];
+                rs += __shfl_xor(rs, 32);
+                if (resc) {
+                    l_run *= alpha;
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) pprev[2 * mt + u][i] = (__bf16)sacc[mt][8 * u + i];
-        }
-        pend = !skip;
-        v_prev = any_keep;
+                    for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+                }
+                l_run += rs;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int u = 0; u < 2; ++u)
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) pprev[2 * mt + u][i] = (__bf16)sacc[mt][8 * u + i];
+            }
+            pend = !skip;
+            v_prev = any_keep;
 
-        // B2: K_{j+1} is in LDS (loads complete in issue order; V_j, issued last, may still fly).
-        if (any_keep) wait_vmem_leave<CI>();
-        else wait_vmem_all();
-        __syncthreads();
+            // B2: K_{j+1} is in LDS (loads complete in issue order; V_j, issued last, may still fly).
+            if (any_keep) wait_vmem_leave<CI>();
+            else wait_vmem_all();
+            __syncthreads();
+        }
     }
+    wait_vmem_all();  // also the copy past the last K block, before the workgroup ends
     if (v_prev) {
-        wait_vmem_all();
         widen_v();
         __syncthreads();
     }
@@ -780,17 +928,21 @@ bsp_status_t check_tensor(const char *name, const bsp_tensor_t *x, int heads, in
 
 typedef void (*kernel_fn)(FwdParams);
 
+template <int IN, int D, int BQ, int BK, bool DENSE>
+kernel_fn pick_mfma2(bool paged, int hpw) {
+    if (hpw == 2) return paged ? fwd_mfma<IN, D, BQ, BK, true, 2, DENSE> : fwd_mfma<IN, D, BQ, BK, false, 2, DENSE>;
+    return paged ? fwd_mfma<IN, D, BQ, BK, true, 1, DENSE> : fwd_mfma<IN, D, BQ, BK, false, 1, DENSE>;
+}
 template <int IN, int D, int BQ, int BK>
-kernel_fn pick_mfma(bool paged, int hpw) {
-    if (hpw == 2) return paged ? fwd_mfma<IN, D, BQ, BK, true, 2> : fwd_mfma<IN, D, BQ, BK, false, 2>;
-    return paged ? fwd_mfma<IN, D, BQ, BK, true, 1> : fwd_mfma<IN, D, BQ, BK, false, 1>;
+kernel_fn pick_mfma(bool paged, int hpw, bool dense) {
+    return dense ? pick_mfma2<IN, D, BQ, BK, true>(paged, hpw) : pick_mfma2<IN, D, BQ, BK, false>(paged, hpw);
 }
 
 template <int D, int BQ, int BK>
-kernel_fn pick_kernel(int dtype, bool paged, int hpw) {
-    if (dtype == BSP_BF16) return pick_mfma<BSP_BF16, D, BQ, BK>(paged, hpw);
+kernel_fn pick_kernel(int dtype, bool paged, int hpw, bool dense) {
+    if (dtype == BSP_BF16) return pick_mfma<BSP_BF16, D, BQ, BK>(paged, hpw, dense);
     if (dtype == BSP_FP8_E4M3) {
-        if constexpr (D == 128) return pick_mfma<BSP_FP8_E4M3, D, BQ, BK>(paged, hpw);
+        if constexpr (D == 128) return pick_mfma<BSP_FP8_E4M3, D, BQ, BK>(paged, hpw, dense);
         return nullptr;  // fp8 kernels are built for head_dim 128 only
     }
     if (dtype == BSP_F32) return paged ? fwd_f32<D, BQ, BK, true> : fwd_f32<D, BQ, BK, false>;
@@ -801,9 +953,9 @@ kernel_fn pick_kernel(int dtype, bool paged, int hpw) {
 // a KV head when the group size is even.
 int heads_per_workgroup(int dtype, int group) { return (dtype != BSP_F32 && group % 2 == 0) ? 2 : 1; }
 
-kernel_fn find_kernel(int dtype, int D, int BQ, int BK, bool paged, int hpw) {
+kernel_fn find_kernel(int dtype, int D, int BQ, int BK, bool paged, int hpw, bool dense) {
 #define BSP_CASE(d, bq, bk) \
-    if (D == d && BQ == bq && BK == bk) return pick_kernel<d, bq, bk>(dtype, paged, hpw);
+    if (D == d && BQ == bq && BK == bk) return pick_kernel<d, bq, bk>(dtype, paged, hpw, dense);
     BSP_CASE(64, 64, 64)
     BSP_CASE(64, 128, 64)
     BSP_CASE(64, 128, 128)
@@ -918,10 +1070,16 @@ bsp_status_t bsp_attn_fwd(const bsp_tensor_t *q, const bsp_tensor_t *k, const bs
             return fail(BSP_ERR_INVALID_ARG, "bitmap holds %lld words, %lld needed", (long long)skip_out->bitmap_words,
                         (long long)words);
     }
+    // K/V copies address a block's rows with 32-bit byte offsets from its first row.
+    {
+        const int64_t es = elem_size(q->dtype);
+        if ((int64_t)block_k * k->stride_token * es >= (1LL << 31) || (int64_t)block_k * v->stride_token * es >= (1LL << 31))
+            return fail(BSP_ERR_UNSUPPORTED, "k/v token stride too large (block_k * stride must stay below 2 GiB)");
+    }
     const int hpw = heads_per_workgroup(q->dtype, n_heads_q / n_heads_kv);
     const int64_t grid64 = T_max * (int64_t)seqs->n_seqs * (n_heads_q / hpw);
     if (grid64 > 0x7fffffffLL) return fail(BSP_ERR_INVALID_ARG, "too many work items");
-    kernel_fn fn = find_kernel(q->dtype, head_dim, block_q, block_k, paged, hpw);
+    kernel_fn fn = find_kernel(q->dtype, head_dim, block_q, block_k, paged, hpw, isinf(lambda));
     if (fn == nullptr)
         return fail(BSP_ERR_UNSUPPORTED, "no kernel for dtype %d, head_dim %d, block_q %d, block_k %d", (int)q->dtype,
                     head_dim, block_q, block_k);
