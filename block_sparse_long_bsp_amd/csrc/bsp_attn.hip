@@ -200,9 +200,13 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // XOR swizzle of the 16-byte chunks of a bf16 LDS row r (row = one key, 2*D bytes).
+// D = 128 (one row per 256-byte bank window): rows 0..15 get sixteen distinct
+// XORs (conflict-free ds_read_b128 of one chunk over 16 rows), and the four
+// rows that one half-wave of a transposing PV read touches (r, r+1, r+2, r+3 for
+// r % 4 == 0) land their four 16-byte chunks in four distinct 64-byte groups.
 template <int D>
 __device__ __forceinline__ int chunk_swz(int r) {
-    if constexpr (D == 128) return 2 * (r & 7) + ((r >> 3) & 1);
+    if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
     else return 2 * ((r >> 1) & 3);
 }
 
@@ -398,8 +402,8 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, 1) fwd_mfma(FwdParams p) {
     // (i' = 0..7). Two transposing reads give lane (dim d, half hh) those 8 keys: in each 16-lane
     // group, source lane i points at key 32mt + 16u + 4hh + i/4 (+8), dims d0 + 4(i%4)..+3. The
     // swizzle depends on the key only through key % 16, so the offset of chunk cc is that of
-    // chunk 0 plus the immediate cc * 16 * VROWB; the second read (keys +8) differs only in the
-    // swizzle bit (D = 128) or not at all (D = 64).
+    // chunk 0 plus the immediate cc * 16 * VROWB; the second read (keys +8) differs only in
+    // swizzle bit 1 (D = 128: chunk offset ^ 32 bytes) or not at all (D = 64).
     int vrd_off[DT];
     {
         const int grp = lane >> 4;
@@ -414,7 +418,7 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, 1) fwd_mfma(FwdParams p) {
     }
     auto vread_at = [&](const char *vbuf, int cc, int dt) -> bf16x8 {
         const int o0 = vrd_off[dt] + cc * 16 * VROWB;
-        const int o8 = (D == 128 ? (vrd_off[dt] ^ 16) : vrd_off[dt]) + cc * 16 * VROWB + 8 * VROWB;
+        const int o8 = (D == 128 ? (vrd_off[dt] ^ 32) : vrd_off[dt]) + cc * 16 * VROWB + 8 * VROWB;
         const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(BSP_LDS(bf16x4, vbuf + o0));
         const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(BSP_LDS(bf16x4, vbuf + o8));
         return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
