@@ -46,6 +46,26 @@ def dense_causal_flops(seqlens, H, D):
     return sum(4.0 * D * H * L * (L + 1) / 2 for L in seqlens)
 
 
+def measured_traffic(workload, dtype, dense):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary of this workload, if it was measured on the current kernel source
+    (else None)."""
+    import hashlib
+
+    import re
+
+    short = re.sub(r"_(bf16|fp8|fp32)$", "", workload)
+    path = os.path.join(ROOT, "profiles", "fwd_mfma_%s_%s_dense_hbm_bytes.json" % (dtype, short))
+    if not dense or not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = os.path.join(ROOT, "block_sparse_long_bsp_amd", "csrc", "bsp_attn.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if rec.get("workload") != workload or rec.get("dtype") != dtype or rec.get("kernel_source_sha256") != sha:
+        return None
+    return float(rec["traffic_bytes_per_launch"])
+
+
 def time_calls(fn, steps, warmup):
     import torch
 
@@ -230,7 +250,7 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": exec_tflops / peak,
-            "traffic": None,
+            "traffic": measured_traffic(w.name, dtype, True),  # HBM bytes per launch (rocprofv3)
             "per_launch": f"{visited} visited + {kept} kept (tile, block) pairs x 2*{w.block_q}*{w.block_k}*{D} "
                           f"FLOP = {exec_flops:.4g} FLOP",
         },
