@@ -246,7 +246,7 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t x) {
 }
 
 template <int IN, int D, int BQ, int BK, bool PAGED, int HPW, bool DENSE>
-__global__ void __launch_bounds__(BQ * 2 * HPW, 1) fwd_mfma(FwdParams p) {
+__global__ void __launch_bounds__(BQ * 2 * HPW, BQ == 64 ? 512 / (BQ * 2 * HPW) : 1) fwd_mfma(FwdParams p) {
     constexpr bool F8 = IN == BSP_FP8_E4M3;
     constexpr int WPH = BQ / 32;     // waves per head
     constexpr int NW = WPH * HPW;    // waves per workgroup
@@ -348,6 +348,8 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, 1) fwd_mfma(FwdParams p) {
     };
     constexpr int CSTEP = NW * KRPK;
     constexpr bool kFixedChunk = CSTEP % 16 == 0;
+    constexpr int kLog2Rpk = KRPK == 8 ? 3 : KRPK == 4 ? 2 : KRPK == 2 ? 1 : 0;
+    static_assert((1 << kLog2Rpk) == KRPK, "rows per copy must be a power of two");
     const int crow0 = w * KRPK + lane / KCPR;
     const int lcK = 16 * ((lane % KCPR) ^ kswz(crow0));
     auto copy_one = [&](const char *src, int64_t stb, int kb, char *dst, bool swz, int i) {
@@ -355,7 +357,21 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, 1) fwd_mfma(FwdParams p) {
         const int kk = min(kb + r, L - 1);
         const int lci = !swz ? 16 * (lane % KCPR) : kFixedChunk ? lcK : 16 * ((lane % KCPR) ^ kswz(r));
         if constexpr (PAGED) {
-            lds_copy16(src + kv_row<PAGED>(p, s, base, kk, stb) + lci, dst + (i * NW + w) * 1024);
+            if (p.page_shift >= kLog2Rpk) {
+                // The instruction's KRPK rows (KRPK-aligned) lie in one page, also after
+                // clamping, so the page id is wave-uniform: a scalar load, which does
+                // not wait behind the copies in flight as a vector load would.
+                const int r0 = __builtin_amdgcn_readfirstlane(min(kb + w * KRPK + i * CSTEP, L - 1));
+                // read-only table through the constant address space: a uniform index
+                // becomes s_load_dword
+                const auto *tbl = (const __attribute__((address_space(4))) int32_t *)p.table;
+                const int pg = __builtin_amdgcn_readfirstlane(tbl[(int64_t)s * p.max_pages + (r0 >> p.page_shift)]);
+                const char *pbase = src + ((int64_t)pg << p.page_shift) * stb;
+                lds_copy16_sb(pbase, (uint32_t)((kk & ((1 << p.page_shift) - 1)) * stb) + (uint32_t)lci,
+                              dst + (i * NW + w) * 1024);
+            } else {
+                lds_copy16(src + kv_row<PAGED>(p, s, base, kk, stb) + lci, dst + (i * NW + w) * 1024);
+            }
         } else {
             const int kb0 = min(kb, L - 1);
             lds_copy16_sb(src + (int64_t)(base + kb0) * stb, (uint32_t)((kk - kb0) * stb) + (uint32_t)lci,
@@ -1074,11 +1090,12 @@ bsp_status_t bsp_attn_fwd(const bsp_tensor_t *q, const bsp_tensor_t *k, const bs
             return fail(BSP_ERR_INVALID_ARG, "bitmap holds %lld words, %lld needed", (long long)skip_out->bitmap_words,
                         (long long)words);
     }
-    // K/V copies address a block's rows with 32-bit byte offsets from its first row.
+    // K/V copies address rows with 32-bit byte offsets from the first row of a block or a page.
     {
         const int64_t es = elem_size(q->dtype);
-        if ((int64_t)block_k * k->stride_token * es >= (1LL << 31) || (int64_t)block_k * v->stride_token * es >= (1LL << 31))
-            return fail(BSP_ERR_UNSUPPORTED, "k/v token stride too large (block_k * stride must stay below 2 GiB)");
+        const int64_t rows = paged && bt->page_size > block_k ? bt->page_size : block_k;
+        if (rows * k->stride_token * es >= (1LL << 31) || rows * v->stride_token * es >= (1LL << 31))
+            return fail(BSP_ERR_UNSUPPORTED, "k/v token stride too large (max(block_k, page_size) * stride must stay below 2 GiB)");
     }
     const int hpw = heads_per_workgroup(q->dtype, n_heads_q / n_heads_kv);
     const int64_t grid64 = T_max * (int64_t)seqs->n_seqs * (n_heads_q / hpw);
