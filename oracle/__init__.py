@@ -50,8 +50,8 @@ def load_library(path: str):
     lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
     lib.bsp_oracle_fwd.restype = ctypes.c_int
-    lib.bsp_oracle_fwd.argtypes = [P, P, P, ctypes.c_int, P, P, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                   ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double, P,
+    lib.bsp_oracle_fwd.argtypes = [P, P, P, ctypes.c_int, P, P, P, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double, P, P,
                                    ctypes.c_int64, P, ctypes.c_int, P, P, P, P, P, P, ctypes.c_int,
                                    ctypes.c_int]
     return lib
@@ -82,7 +82,8 @@ def _ptr(a: Optional[np.ndarray]):
 
 @dataclass
 class OracleResult:
-    """Per-work-item outputs; row r of item w is query tile*block_q + r."""
+    """Per-work-item outputs; row r of item w is query row tile*block_q + r of
+    the sequence's query rows (its chunk, with a cached prefix)."""
     work: np.ndarray        # int32 [n, 3] (seq, head, tile)
     o: np.ndarray           # float64 [n, block_q, D]
     lse: np.ndarray         # float64 [n, block_q]  (NaN past the sequence end)
@@ -101,12 +102,17 @@ def run(q32: np.ndarray, k32: np.ndarray, v32: np.ndarray, cu_seqlens: np.ndarra
         n_heads_q: int, n_heads_kv: int, block_q: int, block_k: int, lam: float,
         work: Optional[np.ndarray] = None, q_scale=None, k_scale=None, v_scale=None,
         forced: Optional[np.ndarray] = None, export_p: bool = False, n_threads: int = 0,
-        j_max: Optional[int] = None) -> OracleResult:
+        j_max: Optional[int] = None, cu_seqlens_k: Optional[np.ndarray] = None,
+        lam_seq: Optional[Sequence[float]] = None) -> OracleResult:
     """Run the oracle on packed varlen inputs.
 
-    ``q32`` [T, Hq, D], ``k32``/``v32`` [T, Hkv, D] hold storage values: float32,
+    ``q32`` [Tq, Hq, D], ``k32``/``v32`` [Tk, Hkv, D] hold storage values: float32,
     bf16 bit patterns (uint16) or fp8 e4m3 codes (uint8), all three of one
     type; the optional per-head scales multiply them (fp8).
+    ``cu_seqlens`` delimits the query rows of each sequence and ``cu_seqlens_k``
+    (default: the same) its keys/values; with Lk > Lq the queries are the last
+    Lq positions of the sequence (chunked prefill against a cached prefix).
+    ``lam_seq`` gives one lambda per sequence (default: ``lam`` for all).
     ``work`` lists (seq, head, tile) triples; default: every tile of every head.
     ``forced`` [n, j_max] uint8 overrides decisions (0 keep, 1 skip, RULE).
     """
@@ -119,9 +125,16 @@ def run(q32: np.ndarray, k32: np.ndarray, v32: np.ndarray, cu_seqlens: np.ndarra
     in_dtype = _IN_DTYPES[q32.dtype]
     cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
     n_seqs = len(cu) - 1
+    cuk = None if cu_seqlens_k is None else np.ascontiguousarray(cu_seqlens_k, dtype=np.int32)
+    if cuk is not None and len(cuk) != n_seqs + 1:
+        raise ValueError("cu_seqlens_k must have n_seqs + 1 entries")
+    lam_arr = None if lam_seq is None else np.ascontiguousarray(lam_seq, dtype=np.float64)
+    if lam_arr is not None and len(lam_arr) != n_seqs:
+        raise ValueError("lam_seq must have one entry per sequence")
     D = q32.shape[2]
     seqlens = np.diff(cu)
-    max_len = int(seqlens.max()) if n_seqs > 0 else 0
+    seqlens_k = seqlens if cuk is None else np.diff(cuk)
+    max_len = int(seqlens_k.max()) if n_seqs > 0 else 0
     if j_max is None:
         j_max = max(1, (max_len + block_k - 1) // block_k)
     if work is None:
@@ -146,8 +159,8 @@ def run(q32: np.ndarray, k32: np.ndarray, v32: np.ndarray, cu_seqlens: np.ndarra
         forced = np.ascontiguousarray(forced, dtype=np.uint8)
         assert forced.shape == (n, j_max)
     rc = lib.bsp_oracle_fwd(_ptr(q32), _ptr(k32), _ptr(v32), in_dtype, _ptr(sc[0]), _ptr(sc[1]), _ptr(sc[2]),
-                            _ptr(cu), n_seqs, n_heads_q, n_heads_kv, D, block_q, block_k, float(lam),
-                            _ptr(work), n, _ptr(forced), j_max, _ptr(o), _ptr(lse), _ptr(skip),
+                            _ptr(cu), _ptr(cuk), n_seqs, n_heads_q, n_heads_kv, D, block_q, block_k, float(lam),
+                            _ptr(lam_arr), _ptr(work), n, _ptr(forced), j_max, _ptr(o), _ptr(lse), _ptr(skip),
                             _ptr(visited), _ptr(mingap), _ptr(p), p_cols, int(n_threads))
     if rc != 0:
         raise ValueError(f"bsp_oracle_fwd failed with code {rc}")

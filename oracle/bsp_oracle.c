@@ -26,6 +26,13 @@
  *     the first block it is -inf, so block 0 is never skipped.
  *   - skipped keys leave both the numerator and the denominator.
  *   - causal masking per sequence: key c is visible to query r iff c <= r.
+ *   - chunked prefill against a cached prefix (the guide's section 3.1 on
+ *     prefill in chunks): a sequence's queries are the LAST Lq of its Lk
+ *     keys (bottom-right alignment), so query row r of the chunk sits at key
+ *     position (Lk - Lq) + r and sees keys 0 .. (Lk - Lq) + r. Lq = Lk is the
+ *     plain prefill.
+ *   - lambda may be given per sequence (the guide's per-request threshold,
+ *     sections 3.3 and 9.3).
  *   - LSE is m + ln(l) over the kept keys, natural log.
  *
  * Arithmetic: every input element is widened exactly to double from its
@@ -44,7 +51,7 @@
 /* forced[] entries: 0 = keep, 1 = skip, anything else = apply the rule. */
 #define BSP_ORACLE_RULE 255
 
-int bsp_oracle_version(void) { return 2; }
+int bsp_oracle_version(void) { return 3; }
 
 /* Storage types of the inputs. */
 enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_FP8_E4M3 = 2 };
@@ -78,10 +85,14 @@ static double elem(const void *base, size_t i, int dtype)
  * q  : [total_tokens][n_heads_q][head_dim]   storage type `in_dtype`
  * k,v: [total_tokens][n_heads_kv][head_dim]  same storage type
  * q_scale/k_scale/v_scale: double per head, or NULL (= 1.0)
- * cu_seqlens: int32 [n_seqs+1], cu[0] = 0, non-decreasing
+ * cu_seqlens: int32 [n_seqs+1], cu[0] = 0, non-decreasing (query rows)
+ * cu_seqlens_k: int32 [n_seqs+1] for the keys/values, or NULL (= cu_seqlens);
+ *             each sequence needs Lk >= Lq
+ * lambda_seq: double [n_seqs] per-sequence lambda, or NULL (= lambda)
  * work: int32 [n_work][3] = (sequence, query head, query tile)
  * forced: uint8 [n_work][j_max] or NULL
- * Outputs, per work item w (row r of the tile is query t*block_q + r):
+ * Outputs, per work item w (row r of the tile is query row t*block_q + r of
+ * the sequence's chunk; key indices are sequence-local):
  *   o_out     double [n_work][block_q][head_dim]  (rows past the sequence: 0)
  *   lse_out   double [n_work][block_q]            (rows past the sequence: NaN)
  *   skip_out  uint8  [n_work][j_max]  1 = visited and skipped, 0 otherwise
@@ -95,9 +106,9 @@ static double elem(const void *base, size_t i, int dtype)
  */
 int bsp_oracle_fwd(const void *q, const void *k, const void *v, int in_dtype,
                    const double *q_scale, const double *k_scale, const double *v_scale,
-                   const int32_t *cu_seqlens, int n_seqs,
+                   const int32_t *cu_seqlens, const int32_t *cu_seqlens_k, int n_seqs,
                    int n_heads_q, int n_heads_kv, int head_dim,
-                   int block_q, int block_k, double lambda,
+                   int block_q, int block_k, double lambda, const double *lambda_seq,
                    const int32_t *work, int64_t n_work,
                    const uint8_t *forced, int j_max,
                    double *o_out, double *lse_out, uint8_t *skip_out, uint8_t *visit_out,
@@ -111,6 +122,9 @@ int bsp_oracle_fwd(const void *q, const void *k, const void *v, int in_dtype,
         return -3;
     if (isnan(lambda) || lambda < 0.0)
         return -4;
+    if (lambda_seq)
+        for (int s = 0; s < n_seqs; ++s)
+            if (isnan(lambda_seq[s]) || lambda_seq[s] < 0.0) return -4;
     if (in_dtype < ORACLE_F32 || in_dtype > ORACLE_FP8_E4M3)
         return -6;
     const int group = n_heads_q / n_heads_kv;
@@ -158,13 +172,22 @@ int bsp_oracle_fwd(const void *q, const void *k, const void *v, int in_dtype,
                 continue;
             }
             const int base = cu_seqlens[s];
-            const int L = cu_seqlens[s + 1] - base;
+            const int L = cu_seqlens[s + 1] - base;                    /* query rows */
+            const int kbase = cu_seqlens_k ? cu_seqlens_k[s] : base;
+            const int Lk = cu_seqlens_k ? cu_seqlens_k[s + 1] - kbase : L;  /* keys */
+            const int off = Lk - L;                 /* query row r sits at key position off + r */
+            const double lam = lambda_seq ? lambda_seq[s] : lambda;
+            if (off < 0) {
+#pragma omp atomic write
+                bad = 1;
+                continue;
+            }
             const int r0 = t * block_q;             /* first query of the tile */
             if (L <= 0 || r0 >= L) continue;        /* empty tile: nothing to do */
             const int r1 = (r0 + block_q < L) ? r0 + block_q : L;
             const int nrows = r1 - r0;
-            /* causal: the last key block touched by the tile holds key r1-1 */
-            const int nblk = (r1 - 1) / block_k + 1;
+            /* causal: the last key block touched by the tile holds key off+r1-1 */
+            const int nblk = (off + r1 - 1) / block_k + 1;
             if (nblk > j_max) {
 #pragma omp atomic write
                 bad = 1;
@@ -189,17 +212,17 @@ int bsp_oracle_fwd(const void *q, const void *k, const void *v, int in_dtype,
 
             for (int j = 0; j < nblk; ++j) {        /* key blocks in ascending order */
                 const int c0 = j * block_k;
-                const int c1 = (c0 + block_k < L) ? c0 + block_k : L;
+                const int c1 = (c0 + block_k < Lk) ? c0 + block_k : Lk;
                 const int nc = c1 - c0;
                 if (visit_out) visit_out[(size_t)w * j_max + j] = 1;
                 for (int c = 0; c < nc; ++c)
                     for (int d = 0; d < D; ++d)
                         kblk[(size_t)c * D + d] =
-                            elem(k, ((size_t)(base + c0 + c) * n_heads_kv + g) * D + d, in_dtype) * sk;
+                            elem(k, ((size_t)(kbase + c0 + c) * n_heads_kv + g) * D + d, in_dtype) * sk;
 
                 /* scaled scores with the causal mask, and the block's local max */
                 for (int r = 0; r < nrows; ++r) {
-                    const int qi = r0 + r;
+                    const int qi = off + r0 + r;        /* key position of this query */
                     double mx = -INFINITY;
                     for (int c = 0; c < nc; ++c) {
                         double val = -INFINITY;
@@ -229,7 +252,7 @@ int bsp_oracle_fwd(const void *q, const void *k, const void *v, int in_dtype,
                 }
                 if (mingap_out) mingap_out[(size_t)w * j_max + j] = mingap;
 
-                int skip = (mingap > lambda);       /* strictly greater */
+                int skip = (mingap > lam);          /* strictly greater */
                 if (forced) {
                     const uint8_t f = forced[(size_t)w * j_max + j];
                     if (f == 0) skip = 0;
@@ -242,7 +265,7 @@ int bsp_oracle_fwd(const void *q, const void *k, const void *v, int in_dtype,
                 for (int c = 0; c < nc; ++c)
                     for (int d = 0; d < D; ++d)
                         vblk[(size_t)c * D + d] =
-                            elem(v, ((size_t)(base + c0 + c) * n_heads_kv + g) * D + d, in_dtype) * sv;
+                            elem(v, ((size_t)(kbase + c0 + c) * n_heads_kv + g) * D + d, in_dtype) * sv;
 
                 for (int r = 0; r < nrows; ++r) {
                     const double mnew = (mloc[r] > m[r]) ? mloc[r] : m[r];
@@ -274,15 +297,15 @@ int bsp_oracle_fwd(const void *q, const void *k, const void *v, int in_dtype,
                 for (int j = 0; j < nblk; ++j) {
                     if (!kept[j]) continue;
                     const int c0 = j * block_k;
-                    const int c1 = (c0 + block_k < L) ? c0 + block_k : L;
+                    const int c1 = (c0 + block_k < Lk) ? c0 + block_k : Lk;
                     for (int r = 0; r < nrows; ++r) {
-                        const int qi = r0 + r;
+                        const int qi = off + r0 + r;
                         for (int c = c0; c < c1 && c < p_cols; ++c) {
                             if (c > qi) continue;
                             double dot = 0.0;
                             for (int d = 0; d < D; ++d)
                                 dot += qrow[(size_t)r * D + d] *
-                                       elem(k, ((size_t)(base + c) * n_heads_kv + g) * D + d, in_dtype) * sk;
+                                       elem(k, ((size_t)(kbase + c) * n_heads_kv + g) * D + d, in_dtype) * sk;
                             p_w[(size_t)r * p_cols + c] = exp(scale * dot - m[r]) / l[r];
                         }
                     }

@@ -433,3 +433,159 @@ def test_invalid_arguments_rejected():
         oracle.run_inputs(inp, 4, 4, float("nan"))
     with pytest.raises(ValueError):
         oracle.run(inp.q32, inp.k32, inp.v32, inp.cu_seqlens, 3, 2, 4, 4, 1.0)
+
+
+# ------------------------------------------ chunked prefill, per-sequence lambda --
+# The queries of a sequence may be the last Lq of its Lk positions (prefill in
+# chunks against a cached prefix, the guide's section 3.1): query row r of the
+# chunk sits at key position (Lk - Lq) + r. Pinned against numpy and brute force
+# written with that offset, and against the plain prefill of the whole sequence.
+
+def chunk_inputs(lk, lq, hq=4, hkv=2, D=16, code=111):
+    """Full-sequence inputs of lengths ``lk`` and their chunks: the last lq[s] rows."""
+    inp = synth.build_inputs(lk, hq, hkv, D, "f32", rho=0.95, n_vert=2, code=code, sink_gain=4.0)
+    cuk = inp.cu_seqlens
+    rows = np.concatenate([np.arange(int(cuk[s + 1]) - lq[s], int(cuk[s + 1])) for s in range(len(lk))]).astype(int)
+    cuq = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
+    return inp, inp.q32[rows], cuq, cuk
+
+
+def dense_scores_kv(q, k, cuq, cuk, hq, hkv):
+    D = q.shape[2]
+    G = hq // hkv
+    out = {}
+    for s in range(len(cuq) - 1):
+        a, b, ka, kb = int(cuq[s]), int(cuq[s + 1]), int(cuk[s]), int(cuk[s + 1])
+        off = (kb - ka) - (b - a)
+        mask = np.arange(kb - ka)[None, :] > (off + np.arange(b - a))[:, None]
+        for h in range(hq):
+            S = (q[a:b, h].astype(np.float64) @ k[ka:kb, h // G].astype(np.float64).T) / math.sqrt(D)
+            S[mask] = -np.inf
+            out[(s, h)] = S
+    return out
+
+
+def naive_kv(q, k, v, cuq, cuk, hq, hkv, keep=None):
+    T, D = q.shape[0], q.shape[2]
+    G = hq // hkv
+    O, LSE = np.zeros((T, hq, D)), np.zeros((hq, T))
+    for (s, h), S in dense_scores_kv(q, k, cuq, cuk, hq, hkv).items():
+        a, b, ka, kb = int(cuq[s]), int(cuq[s + 1]), int(cuk[s]), int(cuk[s + 1])
+        if b == a:
+            continue
+        if keep is not None:
+            S = np.where(keep[(s, h)], S, -np.inf)
+        m = S.max(axis=1, keepdims=True)
+        P = np.exp(S - m)
+        l = P.sum(axis=1, keepdims=True)
+        O[a:b, h] = (P @ v[ka:kb, h // G].astype(np.float64)) / l
+        LSE[h, a:b] = (m + np.log(l))[:, 0]
+    return O, LSE
+
+
+def brute_force_skips_kv(q, k, cuq, cuk, hq, hkv, bq, bk, lam_of):
+    skips, visited, keep = set(), set(), {}
+    for (s, h), S in dense_scores_kv(q, k, cuq, cuk, hq, hkv).items():
+        Lq, Lk = S.shape
+        keep[(s, h)] = np.ones((Lq, Lk), dtype=bool)
+        if Lq == 0:
+            continue
+        off = Lk - Lq
+        J = (Lk + bk - 1) // bk
+        M = np.full((Lq, J), -np.inf)
+        for j in range(J):
+            M[:, j] = S[:, j * bk: min(Lk, (j + 1) * bk)].max(axis=1)
+        for t in range((Lq + bq - 1) // bq):
+            r0, r1 = t * bq, min(Lq, (t + 1) * bq)
+            for j in range((off + r1 - 1) // bk + 1):
+                visited.add((s, h, t, j))
+                prefix = M[r0:r1, :j].max(axis=1) if j > 0 else np.full(r1 - r0, -np.inf)
+                gaps = [np.inf if lm == -np.inf else (-np.inf if pm == -np.inf else pm - lm)
+                        for pm, lm in zip(prefix, M[r0:r1, j])]
+                if min(gaps) > lam_of(s):
+                    skips.add((s, h, t, j))
+                    keep[(s, h)][r0:r1, j * bk: min(Lk, (j + 1) * bk)] = False
+    return skips, visited, keep
+
+
+CHUNK_CASES = [
+    # key lengths, query lengths (the chunk), bq, bk
+    ((37, 130, 1, 64), (37, 50, 1, 1), 16, 16),
+    ((300, 129), (300, 129), 32, 32),          # no cached prefix: plain prefill
+    ((300, 257, 90), (45, 1, 90), 32, 16),
+    ((200,), (0,), 16, 16),                    # empty chunk
+]
+
+
+def _scatter_kv(res, cuq, hq):
+    return oracle.scatter(res, cuq, hq)
+
+
+@pytest.mark.parametrize("case", CHUNK_CASES)
+def test_chunked_dense_limit_equals_naive_softmax(case):
+    lk, lq, bq, bk = case
+    inp, qc, cuq, cuk = chunk_inputs(lk, lq)
+    res = oracle.run(qc, inp.k32, inp.v32, cuq, 4, 2, bq, bk, math.inf, cu_seqlens_k=cuk)
+    assert res.skip.sum() == 0
+    O, LSE = _scatter_kv(res, cuq, 4)
+    On, LSEn = naive_kv(qc, inp.k32, inp.v32, cuq, cuk, 4, 2)
+    if O.size:
+        assert np.abs(O - On).max() < 1e-12 and np.abs(LSE - LSEn).max() < 1e-12
+
+
+@pytest.mark.parametrize("case", CHUNK_CASES)
+@pytest.mark.parametrize("lam", [0.0, 1.5])
+def test_chunked_skip_set_and_kept_keys_match_brute_force(case, lam):
+    lk, lq, bq, bk = case
+    inp, qc, cuq, cuk = chunk_inputs(lk, lq)
+    res = oracle.run(qc, inp.k32, inp.v32, cuq, 4, 2, bq, bk, lam, cu_seqlens_k=cuk)
+    skips, visited, keep = brute_force_skips_kv(qc, inp.k32, cuq, cuk, 4, 2, bq, bk, lambda s: lam)
+    assert oracle_sets(res) == (skips, visited)
+    O, LSE = _scatter_kv(res, cuq, 4)
+    On, LSEn = naive_kv(qc, inp.k32, inp.v32, cuq, cuk, 4, 2, keep=keep)
+    if O.size:
+        assert np.abs(O - On).max() < 1e-12 and np.abs(LSE - LSEn).max() < 1e-12
+
+
+@pytest.mark.parametrize("prefix_tiles", [0, 1, 3])
+def test_chunk_after_whole_tiles_equals_rows_of_full_prefill(prefix_tiles):
+    # With a cached prefix of whole query tiles, the chunk's tiles are the full
+    # prefill's later tiles: same rows, same blocks, same decisions, same numbers.
+    bq, bk, L = 32, 16, 150
+    P = prefix_tiles * bq
+    inp = synth.build_inputs((L,), 4, 2, 16, "f32", rho=0.95, n_vert=3, code=112, sink_gain=4.0)
+    for lam in (0.5, 2.0, math.inf):
+        full = oracle.run_inputs(inp, bq, bk, lam)
+        cuq = np.array([0, L - P], np.int32)
+        ch = oracle.run(inp.q32[P:], inp.k32, inp.v32, cuq, 4, 2, bq, bk, lam, cu_seqlens_k=inp.cu_seqlens)
+        for w, (s, h, t) in enumerate(ch.work):
+            wf = [i for i, x in enumerate(full.work) if tuple(x) == (s, h, t + prefix_tiles)][0]
+            assert np.array_equal(ch.o[w], full.o[wf])
+            assert np.array_equal(ch.lse[w], full.lse[wf], equal_nan=True)
+            assert np.array_equal(ch.skip[w], full.skip[wf])
+
+
+def test_lambda_per_sequence_equals_separate_runs():
+    lk, lq = (120, 90, 64, 77), (120, 40, 64, 1)
+    lams = [0.0, 1.0, math.inf, 3.0]
+    inp, qc, cuq, cuk = chunk_inputs(lk, lq, code=113)
+    res = oracle.run(qc, inp.k32, inp.v32, cuq, 4, 2, 16, 16, 99.0, cu_seqlens_k=cuk, lam_seq=lams)
+    skips, visited, keep = brute_force_skips_kv(qc, inp.k32, cuq, cuk, 4, 2, 16, 16, lambda s: lams[s])
+    assert oracle_sets(res) == (skips, visited)
+    for s in range(len(lk)):
+        one_q = qc[cuq[s]:cuq[s + 1]]
+        one_kv = slice(int(cuk[s]), int(cuk[s + 1]))
+        r1 = oracle.run(one_q, inp.k32[one_kv], inp.v32[one_kv], np.array([0, lq[s]], np.int32), 4, 2, 16, 16,
+                        lams[s], cu_seqlens_k=np.array([0, lk[s]], np.int32))
+        items = [w for w, x in enumerate(res.work) if x[0] == s]
+        assert np.array_equal(res.o[items], r1.o)
+        assert np.array_equal(res.skip[items][:, : r1.skip.shape[1]], r1.skip)
+
+
+def test_chunked_and_per_sequence_arguments_rejected():
+    inp, qc, cuq, cuk = chunk_inputs((40, 20), (10, 20))
+    q35 = np.zeros((35,) + qc.shape[1:], np.float32)
+    with pytest.raises(ValueError):   # a chunk longer than its sequence
+        oracle.run(q35, inp.k32, inp.v32, np.array([0, 10, 35], np.int32), 4, 2, 8, 8, 1.0, cu_seqlens_k=cuk)
+    with pytest.raises(ValueError):   # a negative per-sequence lambda
+        oracle.run(qc, inp.k32, inp.v32, cuq, 4, 2, 8, 8, 1.0, cu_seqlens_k=cuk, lam_seq=[1.0, -1.0])
