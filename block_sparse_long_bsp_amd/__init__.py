@@ -27,8 +27,12 @@ LIB_PATH = os.environ.get("BSP_ATTN_LIB") or os.path.join(_PKG, "libbsp_attn.so"
 BSP_OK, BSP_ERR_INVALID_ARG, BSP_ERR_UNSUPPORTED, BSP_ERR_HIP, BSP_ERR_DEVICE = range(5)
 BSP_F32, BSP_BF16, BSP_FP8_E4M3 = 0, 1, 2
 
-EXPORTED = ("bsp_attn_fwd", "bsp_skip_bitmap_words", "bsp_status_string", "bsp_last_error_detail",
-            "bsp_version")
+EXPORTED = ("bsp_attn_fwd", "bsp_attn_fwd_ex", "bsp_skip_bitmap_words", "bsp_skip_bitmap_words_kv",
+            "bsp_status_string", "bsp_last_error_detail", "bsp_version")
+
+# ablation switches of bsp_attn_fwd_ex (results unchanged, only the work done changes)
+FLAG_LOAD_SKIPPED_V = 1  # copy V also for blocks every query head of the workgroup skips
+FLAG_EXP_SKIPPED = 2     # compute (and drop) the exponentials of skipped blocks
 
 
 class BspError(RuntimeError):
@@ -57,6 +61,12 @@ class SkipOut(ctypes.Structure):
                 ("visited_count", ctypes.c_void_p)]
 
 
+class Options(ctypes.Structure):
+    _fields_ = [("cu_seqlens_k", ctypes.c_void_p), ("max_seqlen_k", ctypes.c_int32), ("lambda_per_seq", ctypes.c_void_p),
+                ("skip_count_per_seq", ctypes.c_void_p), ("visited_count_per_seq", ctypes.c_void_p),
+                ("flags", ctypes.c_uint32)]
+
+
 _lib = None
 
 
@@ -73,8 +83,12 @@ def load_library(path: str = LIB_PATH):
     lib.bsp_attn_fwd.restype = ctypes.c_int
     lib.bsp_attn_fwd.argtypes = [P, P, P, P, P, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                  ctypes.c_int, ctypes.c_float, P, P]
+    lib.bsp_attn_fwd_ex.restype = ctypes.c_int
+    lib.bsp_attn_fwd_ex.argtypes = lib.bsp_attn_fwd.argtypes + [P]
     lib.bsp_skip_bitmap_words.restype = ctypes.c_int64
     lib.bsp_skip_bitmap_words.argtypes = [ctypes.c_int] * 5
+    lib.bsp_skip_bitmap_words_kv.restype = ctypes.c_int64
+    lib.bsp_skip_bitmap_words_kv.argtypes = [ctypes.c_int] * 6
     lib.bsp_status_string.restype = ctypes.c_char_p
     lib.bsp_status_string.argtypes = [ctypes.c_int]
     lib.bsp_last_error_detail.restype = ctypes.c_char_p
@@ -97,17 +111,26 @@ def skip_bitmap_words(n_heads_q: int, n_seqs: int, max_seqlen: int, block_q: int
     return int(load_library().bsp_skip_bitmap_words(n_heads_q, n_seqs, max_seqlen, block_q, block_k))
 
 
+def skip_bitmap_words_kv(n_heads_q: int, n_seqs: int, max_seqlen_q: int, max_seqlen_k: int, block_q: int,
+                         block_k: int) -> int:
+    return int(load_library().bsp_skip_bitmap_words_kv(n_heads_q, n_seqs, max_seqlen_q, max_seqlen_k, block_q,
+                                                       block_k))
+
+
 def fwd_raw(q: Tensor, k: Tensor, v: Tensor, o: Tensor, lse_ptr: int, seqs: Seqs, block_table: Optional[BlockTable],
             n_heads_q: int, n_heads_kv: int, head_dim: int, block_q: int, block_k: int, lam: float,
-            skip_out: Optional[SkipOut], stream_ptr: int) -> int:
-    """Direct call of the C entry point with prepared descriptors; returns the status."""
+            skip_out: Optional[SkipOut], stream_ptr: int, options: Optional[Options] = None) -> int:
+    """Direct call of the C entry point (``bsp_attn_fwd``, or ``bsp_attn_fwd_ex``
+    when options are given) with prepared descriptors; returns the status."""
     lib = load_library()
     bt = ctypes.byref(block_table) if block_table is not None else None
     so = ctypes.byref(skip_out) if skip_out is not None else None
-    return int(lib.bsp_attn_fwd(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), ctypes.byref(o),
-                                ctypes.c_void_p(lse_ptr or None), ctypes.byref(seqs), bt, n_heads_q, n_heads_kv,
-                                head_dim, block_q, block_k, ctypes.c_float(lam), so,
-                                ctypes.c_void_p(stream_ptr or None)))
+    args = (ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), ctypes.byref(o), ctypes.c_void_p(lse_ptr or None),
+            ctypes.byref(seqs), bt, n_heads_q, n_heads_kv, head_dim, block_q, block_k, ctypes.c_float(lam), so,
+            ctypes.c_void_p(stream_ptr or None))
+    if options is None:
+        return int(lib.bsp_attn_fwd(*args))
+    return int(lib.bsp_attn_fwd_ex(*args, ctypes.byref(options)))
 
 
 _DT = {torch.float32: BSP_F32, torch.bfloat16: BSP_BF16}
@@ -132,14 +155,25 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Ten
         v_scale: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
         lse: Optional[torch.Tensor] = None, bitmap: Optional[torch.Tensor] = None,
         skip_count: Optional[torch.Tensor] = None, visited_count: Optional[torch.Tensor] = None,
-        want_bitmap: bool = True, want_lse: bool = True) -> Tuple[torch.Tensor, ...]:
+        want_bitmap: bool = True, want_lse: bool = True, cu_seqlens_k: Optional[torch.Tensor] = None,
+        max_seqlen_k: Optional[int] = None, lam_per_seq: Optional[torch.Tensor] = None,
+        seq_skip_count: Optional[torch.Tensor] = None, seq_visited_count: Optional[torch.Tensor] = None,
+        flags: int = 0) -> Tuple[torch.Tensor, ...]:
     """Block-sparse causal prefill attention on the current stream.
 
-    q [T, Hq, D]; k, v [T, Hkv, D] packed, or paged [n_pages, page_size, Hkv, D]
+    q [Tq, Hq, D]; k, v [Tk, Hkv, D] packed, or paged [n_pages, page_size, Hkv, D]
     with ``block_table`` int32 [n_seqs, max_pages]. cu_seqlens int32 [n_seqs+1]
     on the device. Returns (o, lse, bitmap, skip_count, visited_count); the
     optional outputs are None when not requested. Output buffers may be passed
     in to avoid allocation.
+
+    Options (``bsp_attn_fwd_ex``): ``cu_seqlens_k`` (device int32, with
+    ``max_seqlen_k``) gives each sequence Lk >= Lq keys of which its queries
+    are the last Lq (chunked prefill against a cached prefix; Lq = 1 is a
+    decoding step); ``lam_per_seq`` (device float32 [n_seqs]) replaces ``lam``
+    per sequence; ``seq_skip_count`` / ``seq_visited_count`` (device int64
+    [n_seqs], filled in place) count skipped / visited pairs per sequence;
+    ``flags`` holds the FLAG_* ablation switches.
     """
     load_library()
     if q.device.type != "cuda":
@@ -156,12 +190,15 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Ten
         k3, v3 = k, v
     Hkv = k3.shape[1]
     n_seqs = cu_seqlens.numel() - 1
+    use_ex = (cu_seqlens_k is not None or lam_per_seq is not None or seq_skip_count is not None
+              or seq_visited_count is not None or flags != 0)
+    max_k = int(max_seqlen_k) if cu_seqlens_k is not None else int(max_seqlen)
     odt = torch.float32 if q.dtype == torch.float32 else torch.bfloat16
     if out is None:
         out = torch.empty((T, Hq, D), dtype=odt, device=q.device)
     if want_lse and lse is None:
         lse = torch.empty((Hq, T), dtype=torch.float32, device=q.device)
-    words = skip_bitmap_words(Hq, n_seqs, max_seqlen, block_q, block_k) if n_seqs > 0 else 0
+    words = skip_bitmap_words_kv(Hq, n_seqs, max_seqlen, max_k, block_q, block_k) if n_seqs > 0 else 0
     if want_bitmap and bitmap is None:
         bitmap = torch.empty((max(words, 1),), dtype=torch.int32, device=q.device)
     if skip_count is None:
@@ -173,20 +210,31 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Ten
     so = SkipOut(bitmap.data_ptr() if bitmap is not None else None, bitmap.numel() if bitmap is not None else 0,
                  skip_count.data_ptr(), visited_count.data_ptr())
     stream = torch.cuda.current_stream(q.device).cuda_stream
+    opts = None
+    if use_ex:
+        for name, x, dt in (("cu_seqlens_k", cu_seqlens_k, torch.int32), ("lam_per_seq", lam_per_seq, torch.float32),
+                            ("seq_skip_count", seq_skip_count, torch.int64),
+                            ("seq_visited_count", seq_visited_count, torch.int64)):
+            if x is not None and (x.dtype != dt or not x.is_contiguous() or x.device != q.device):
+                raise ValueError(f"{name} must be a contiguous {dt} tensor on {q.device}")
+        opts = Options(cu_seqlens_k.data_ptr() if cu_seqlens_k is not None else None, max_k,
+                       lam_per_seq.data_ptr() if lam_per_seq is not None else None,
+                       seq_skip_count.data_ptr() if seq_skip_count is not None else None,
+                       seq_visited_count.data_ptr() if seq_visited_count is not None else None, int(flags))
     st = fwd_raw(_desc(q, q_scale), _desc(k3, k_scale), _desc(v3, v_scale), _desc(out), lse.data_ptr() if lse is not None else 0,
-                 seqs, bt, Hq, Hkv, D, block_q, block_k, float(lam), so, stream)
+                 seqs, bt, Hq, Hkv, D, block_q, block_k, float(lam), so, stream, opts)
     if st != BSP_OK:
         raise BspError(st, last_error_detail())
     return out, lse, bitmap, skip_count, visited_count
 
 
 def unpack_bitmap(bitmap: torch.Tensor, n_heads_q: int, n_seqs: int, max_seqlen: int, block_q: int,
-                  block_k: int):
+                  block_k: int, max_seqlen_k: Optional[int] = None):
     """Host-side view of the bitmap as a bool numpy array [Hq, n_seqs, T_max, J_max]."""
     import numpy as np
 
     T = (max_seqlen + block_q - 1) // block_q
-    J = (max_seqlen + block_k - 1) // block_k
+    J = ((max_seqlen if max_seqlen_k is None else max_seqlen_k) + block_k - 1) // block_k
     W = (J + 31) // 32
     words = bitmap[: n_heads_q * n_seqs * T * W].cpu().numpy().view(np.uint32).reshape(n_heads_q, n_seqs, T, W)
     bits = ((words[..., :, None] >> np.arange(32, dtype=np.uint32)) & 1).astype(bool)

@@ -73,6 +73,12 @@ struct FwdParams {
     const float *q_scale, *k_scale, *v_scale;
     float scale;                    // 1 / sqrt(head_dim)
     float lam;                      // lambda in natural-log units (+inf: dense)
+    // chunked prefill: key/value bounds per sequence (NULL: same as cu); the
+    // queries of a sequence are its last Lq of Lk positions
+    const int32_t *cu_k;
+    const float *lam_seq;           // lambda per sequence, or NULL
+    unsigned long long *seq_skip, *seq_visited;  // counts per sequence, or NULL
+    uint32_t flags;                 // BSP_FLAG_* ablation switches
 };
 
 constexpr float kLn2 = 0.69314718055994530942f;
@@ -114,7 +120,7 @@ __device__ __forceinline__ void decode_item(const FwdParams &p, int &s, int &t, 
 template <bool PAGED>
 __device__ __forceinline__ int64_t kv_row(const FwdParams &p, int s, int base, int kk, int64_t st) {
     if constexpr (PAGED) {
-        const int pg = p.table[(int64_t)s * p.max_pages + (kk >> p.page_shift)];
+        const int pg = p.table[(int64_t)s * p.max_pages + min(kk >> p.page_shift, p.max_pages - 1)];
         const int64_t slot = ((int64_t)pg << p.page_shift) + (kk & ((1 << p.page_shift) - 1));
         return slot * st;
     } else {
@@ -150,7 +156,8 @@ __device__ __forceinline__ void log_decision(const FwdParams &p, SkipLog &lg, in
         ++lg.nskip;
     }
     if ((j & 31) == 31 || j == nblk - 1) {
-        if (p.bitmap != nullptr && writer) p.bitmap[row * p.W + (j >> 5)] = lg.word;
+        // (j >> 5) < W unless the caller's max_seqlen(_k) understates a sequence: never write past the row
+        if (p.bitmap != nullptr && writer && (j >> 5) < p.W) p.bitmap[row * p.W + (j >> 5)] = lg.word;
         lg.word = 0;
     }
 }
@@ -246,7 +253,7 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t x) {
 }
 
 template <int IN, int D, int BQ, int BK, bool PAGED, int HPW, bool DENSE>
-__global__ void __launch_bounds__(BQ * 2 * HPW, BQ == 64 ? 512 / (BQ * 2 * HPW) : 1) fwd_mfma(FwdParams p) {
+__global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) fwd_mfma(FwdParams p) {
     constexpr bool F8 = IN == BSP_FP8_E4M3;
     constexpr int WPH = BQ / 32;     // waves per head
     constexpr int NW = WPH * HPW;    // waves per workgroup
@@ -273,8 +280,12 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, BQ == 64 ? 512 / (BQ * 2 * HPW) 
     int s, t, hp;
     decode_item(p, s, t, hp);  // hp: index of the head group served by this workgroup
     const int base = p.cu[s];
-    const int L = p.cu[s + 1] - base;
+    const int L = p.cu[s + 1] - base;  // query rows of the sequence (its chunk)
     if (t * BQ >= L) return;  // tile past the end of this sequence (bitmap row stays zero)
+    const int kbase = p.cu_k ? p.cu_k[s] : base;
+    const int Lk = p.cu_k ? p.cu_k[s + 1] - kbase : L;  // keys of the sequence
+    const int off = Lk - L;            // query row r sits at key position off + r
+    if (off < 0) return;               // a chunk longer than its sequence: caller error, nothing written
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -286,20 +297,26 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, BQ == 64 ? 512 / (BQ * 2 * HPW) 
     const int hh = lane >> 5;
     const int g = h / p.G;
     const int r1 = min((t + 1) * BQ, L);
-    const int nblk = (r1 - 1) / BK + 1;
+    const int nblk = (off + r1 - 1) / BK + 1;  // causal: up to the block of key position off + r1 - 1
     const int q0 = t * BQ + wq * 32;
     const int qrow = q0 + ln;
     const bool valid = qrow < L;
+    const int qpos = off + qrow;       // key position of this lane's query
     const int64_t bm_row = ((int64_t)h * p.n_seqs + s) * p.T_max + t;
     constexpr bool dense = DENSE;  // lambda = +inf: every block is kept, no vote
     float c = p.c_log2;           // raw score -> base-2 exponent
     float lam_raw = p.lam_raw;    // lambda in raw score units
     float osc = 1.f;              // output scale
+    float sqk = 1.f;
     if constexpr (F8) {
-        const float sqk = p.q_scale[h] * p.k_scale[g];
+        sqk = p.q_scale[h] * p.k_scale[g];
         c = p.c_log2 * sqk;
         if (!dense) lam_raw = p.lam / (p.scale * sqk);
         osc = p.v_scale[g];
+    }
+    if (!dense && p.lam_seq != nullptr) {
+        const float ls = p.lam_seq[s];
+        lam_raw = ls == INFINITY ? INFINITY : ls / (p.scale * sqk);
     }
 
     const char *kg = (const char *)p.k + (int64_t)g * p.k_sh * ES;
@@ -354,27 +371,29 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, BQ == 64 ? 512 / (BQ * 2 * HPW) 
     const int lcK = 16 * ((lane % KCPR) ^ kswz(crow0));
     auto copy_one = [&](const char *src, int64_t stb, int kb, char *dst, bool swz, int i) {
         const int r = crow0 + i * CSTEP;
-        const int kk = min(kb + r, L - 1);
+        const int kk = min(kb + r, Lk - 1);
         const int lci = !swz ? 16 * (lane % KCPR) : kFixedChunk ? lcK : 16 * ((lane % KCPR) ^ kswz(r));
         if constexpr (PAGED) {
-            if (p.page_shift >= kLog2Rpk) {
+            // (more than 4 copies per wave hold too many page bases in scalar registers)
+            if (CI <= 4 && p.page_shift >= kLog2Rpk) {
                 // The instruction's KRPK rows (KRPK-aligned) lie in one page, also after
                 // clamping, so the page id is wave-uniform: a scalar load, which does
                 // not wait behind the copies in flight as a vector load would.
-                const int r0 = __builtin_amdgcn_readfirstlane(min(kb + w * KRPK + i * CSTEP, L - 1));
+                const int r0 = __builtin_amdgcn_readfirstlane(min(kb + w * KRPK + i * CSTEP, Lk - 1));
                 // read-only table through the constant address space: a uniform index
                 // becomes s_load_dword
                 const auto *tbl = (const __attribute__((address_space(4))) int32_t *)p.table;
-                const int pg = __builtin_amdgcn_readfirstlane(tbl[(int64_t)s * p.max_pages + (r0 >> p.page_shift)]);
+                const int pg = __builtin_amdgcn_readfirstlane(
+                    tbl[(int64_t)s * p.max_pages + min(r0 >> p.page_shift, p.max_pages - 1)]);
                 const char *pbase = src + ((int64_t)pg << p.page_shift) * stb;
                 lds_copy16_sb(pbase, (uint32_t)((kk & ((1 << p.page_shift) - 1)) * stb) + (uint32_t)lci,
                               dst + (i * NW + w) * 1024);
             } else {
-                lds_copy16(src + kv_row<PAGED>(p, s, base, kk, stb) + lci, dst + (i * NW + w) * 1024);
+                lds_copy16(src + kv_row<PAGED>(p, s, kbase, kk, stb) + lci, dst + (i * NW + w) * 1024);
             }
         } else {
-            const int kb0 = min(kb, L - 1);
-            lds_copy16_sb(src + (int64_t)(base + kb0) * stb, (uint32_t)((kk - kb0) * stb) + (uint32_t)lci,
+            const int kb0 = min(kb, Lk - 1);
+            lds_copy16_sb(src + (int64_t)(kbase + kb0) * stb, (uint32_t)((kk - kb0) * stb) + (uint32_t)lci,
                           dst + (i * NW + w) * 1024);
         }
     };
@@ -504,13 +523,13 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, BQ == 64 ? 512 / (BQ * 2 * HPW) 
                 SCHED_FENCE();
             }
         }
-        if (kb + BK - 1 > q0) {  // causal mask (only where the block reaches past this wave's first query)
+        if (kb + BK - 1 > off + q0) {  // causal mask (only where the block reaches past this wave's first query)
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int key = kb + 32 * mt + 8 * (i >> 2) + 4 * hh + (i & 3);
-                    if (key > qrow) sacc[mt][i] = -INFINITY;
+                    if (key > qpos) sacc[mt][i] = -INFINITY;
                 }
         }
         float m = -INFINITY;
@@ -666,18 +685,20 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, BQ == 64 ? 512 / (BQ * 2 * HPW) 
                 any_keep = any_keep || !sk;
             }
             if (wq == 0) log_decision(p, lg, bm_row, j, nblk, skip, lane == 0);
+            // ablation: copy V also for blocks every head skips
+            any_keep = any_keep || (p.flags & BSP_FLAG_LOAD_SKIPPED_V) != 0;
             if (any_keep) {
                 if constexpr (F8) copy_block(vg, vstb, kb, sV8, false);
                 else copy_block(vg, vstb, kb, sV[cur], true);
             }
-            // softmax of block j, then the pending PV of the previous kept block
-            // exponentials in place, then the pending PV, then row sum, rescale and
+            // Exponentials in place, then the pending PV, then row sum, rescale and
             // the bf16 probabilities (the fused order of the dense loop does not fit
-            // the registers next to the skip branches)
+            // the registers next to the skip branches). Ablation: a skipped block's
+            // exponentials are computed against the unchanged reference and dropped.
             float alpha = 1.f;
             bool resc = false;
-            if (!skip) {
-                const float mc = new_reference(mloc, alpha, resc);
+            if (!skip || (p.flags & BSP_FLAG_EXP_SKIPPED) != 0) {
+                const float mc = skip ? m_ref * c : new_reference(mloc, alpha, resc);
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -738,8 +759,11 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, BQ == 64 ? 512 / (BQ * 2 * HPW) 
     if (wq == 0 && lane == 0) {
         if (p.skip_count) atomicAdd(&p.skip_count[h], (unsigned long long)lg.nskip);
         if (p.visited_count) atomicAdd(&p.visited_count[h], (unsigned long long)nblk);
+        if (p.seq_skip) atomicAdd(&p.seq_skip[s], (unsigned long long)lg.nskip);
+        if (p.seq_visited) atomicAdd(&p.seq_visited[s], (unsigned long long)nblk);
     }
 }
+
 // ---------------------------------------------------------------------------
 // fp32 kernel: QK^T and PV on v_mfma_f32_32x32x2_f32 (one element per lane
 // per operand, so V needs no transpose).
@@ -759,8 +783,12 @@ __global__ void __launch_bounds__(BQ * 2) fwd_f32(FwdParams p) {
     int s, t, h;
     decode_item(p, s, t, h);
     const int base = p.cu[s];
-    const int L = p.cu[s + 1] - base;
+    const int L = p.cu[s + 1] - base;  // query rows of the sequence (its chunk)
     if (t * BQ >= L) return;
+    const int kbase = p.cu_k ? p.cu_k[s] : base;
+    const int Lk = p.cu_k ? p.cu_k[s + 1] - kbase : L;  // keys
+    const int off = Lk - L;            // query row r sits at key position off + r
+    if (off < 0) return;               // caller error: nothing written
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -769,11 +797,14 @@ __global__ void __launch_bounds__(BQ * 2) fwd_f32(FwdParams p) {
     const int hh = lane >> 5;
     const int g = h / p.G;
     const int r1 = min((t + 1) * BQ, L);
-    const int nblk = (r1 - 1) / BK + 1;
+    const int nblk = (off + r1 - 1) / BK + 1;
     const int q0 = t * BQ + w * 32;
     const int qrow = q0 + ln;
     const bool valid = qrow < L;
+    const int qpos = off + qrow;
     const int64_t bm_row = ((int64_t)h * p.n_seqs + s) * p.T_max + t;
+    const float lam_raw = p.lam_seq == nullptr ? p.lam_raw
+                          : (p.lam_seq[s] == INFINITY ? INFINITY : p.lam_seq[s] / p.scale);
 
     const float *qg = (const float *)p.q;
     const float *kg = (const float *)p.k;
@@ -800,7 +831,7 @@ __global__ void __launch_bounds__(BQ * 2) fwd_f32(FwdParams p) {
             const int c4 = c % (D / 4);
             const int kk = kb + r;
             f32x4 x{};
-            if (kk < L) x = *(const f32x4 *)(kg + kv_row<PAGED>(p, s, base, kk, p.k_st) + (int64_t)g * p.k_sh + 4 * c4);
+            if (kk < Lk) x = *(const f32x4 *)(kg + kv_row<PAGED>(p, s, kbase, kk, p.k_st) + (int64_t)g * p.k_sh + 4 * c4);
 #pragma unroll
             for (int e = 0; e < 4; ++e) sK[r * STR + 4 * c4 + e] = x[e];
         }
@@ -815,13 +846,13 @@ __global__ void __launch_bounds__(BQ * 2) fwd_f32(FwdParams p) {
                 acc = __builtin_amdgcn_mfma_f32_32x32x2f32(sK[(32 * mt + ln) * STR + 2 * ks + hh], qf[ks], acc, 0, 0, 0);
             sacc[mt] = acc;
         }
-        if (kb + BK - 1 > q0) {
+        if (kb + BK - 1 > off + q0) {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int key = kb + 32 * mt + 8 * (i >> 2) + 4 * hh + (i & 3);
-                    if (key > qrow) sacc[mt][i] = -INFINITY;
+                    if (key > qpos) sacc[mt][i] = -INFINITY;
                 }
         }
         float mloc = wave_max16(sacc[0]);
@@ -829,7 +860,7 @@ __global__ void __launch_bounds__(BQ * 2) fwd_f32(FwdParams p) {
         for (int mt = 1; mt < MT; ++mt) mloc = fmaxf(mloc, wave_max16(sacc[mt]));
         mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
 
-        const bool ok = !valid || (mloc == -INFINITY) || (m_run - mloc > p.lam_raw);
+        const bool ok = !valid || (mloc == -INFINITY) || (m_run - mloc > lam_raw);
         const int wall = __all(ok);
         if (lane == 0) sVote[w] = wall;
         __syncthreads();
@@ -837,16 +868,28 @@ __global__ void __launch_bounds__(BQ * 2) fwd_f32(FwdParams p) {
 #pragma unroll
         for (int x = 0; x < NW; ++x) skip = skip && (sVote[x] != 0);
         log_decision(p, lg, bm_row, j, nblk, skip, tid == 0);
-        if (skip) continue;
-
-        for (int c = tid; c < BK * D / 4; c += NT) {
-            const int r = c / (D / 4);
-            const int c4 = c % (D / 4);
-            const int kk = kb + r;
-            f32x4 x{};
-            if (kk < L) x = *(const f32x4 *)(vg + kv_row<PAGED>(p, s, base, kk, p.v_st) + (int64_t)g * p.v_sh + 4 * c4);
+        if (!skip || (p.flags & BSP_FLAG_LOAD_SKIPPED_V) != 0) {
+            for (int c = tid; c < BK * D / 4; c += NT) {
+                const int r = c / (D / 4);
+                const int c4 = c % (D / 4);
+                const int kk = kb + r;
+                f32x4 x{};
+                if (kk < Lk) x = *(const f32x4 *)(vg + kv_row<PAGED>(p, s, kbase, kk, p.v_st) + (int64_t)g * p.v_sh + 4 * c4);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sV[r * STR + 4 * c4 + e] = x[e];
+                for (int e = 0; e < 4; ++e) sV[r * STR + 4 * c4 + e] = x[e];
+            }
+        }
+        if (skip) {
+            if ((p.flags & BSP_FLAG_EXP_SKIPPED) != 0) {  // ablation: exponentials computed and dropped
+                const float mc = m_run * p.c_log2;
+                float sink = 0.f;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) sink += __builtin_amdgcn_exp2f(fmaf(sacc[mt][i], p.c_log2, -mc));
+                asm volatile("" ::"v"(sink));
+            }
+            continue;
         }
 
         const float m_new = fmaxf(m_run, mloc);
@@ -898,20 +941,27 @@ __global__ void __launch_bounds__(BQ * 2) fwd_f32(FwdParams p) {
     if (tid == 0) {
         if (p.skip_count) atomicAdd(&p.skip_count[h], (unsigned long long)lg.nskip);
         if (p.visited_count) atomicAdd(&p.visited_count[h], (unsigned long long)nblk);
+        if (p.seq_skip) atomicAdd(&p.seq_skip[s], (unsigned long long)lg.nskip);
+        if (p.seq_visited) atomicAdd(&p.seq_visited[s], (unsigned long long)nblk);
     }
 }
 
 // Zero the bitmap and the counters ahead of the main kernel (a plain fill
 // kernel keeps the call free of memset nodes).
 __global__ void __launch_bounds__(256) fill_outputs(uint32_t *bitmap, int64_t words, unsigned long long *c0,
-                                                    unsigned long long *c1, int n_heads) {
+                                                    unsigned long long *c1, int n_heads, unsigned long long *c2,
+                                                    unsigned long long *c3, int n_seqs) {
     const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     if (bitmap)
         for (int64_t i = i0; i < words; i += stride) bitmap[i] = 0u;
-    if (i0 < n_heads) {
-        if (c0) c0[i0] = 0ull;
-        if (c1) c1[i0] = 0ull;
+    for (int64_t i = i0; i < n_heads; i += stride) {
+        if (c0) c0[i] = 0ull;
+        if (c1) c1[i] = 0ull;
+    }
+    for (int64_t i = i0; i < n_seqs; i += stride) {
+        if (c2) c2[i] = 0ull;
+        if (c3) c3[i] = 0ull;
     }
 }
 
@@ -1031,19 +1081,45 @@ const char *bsp_status_string(int status) {
 
 const char *bsp_last_error_detail(void) { return g_detail; }
 
-int64_t bsp_skip_bitmap_words(int n_heads_q, int n_seqs, int max_seqlen, int block_q, int block_k) {
-    if (n_heads_q <= 0 || n_seqs < 0 || max_seqlen < 0 || block_q <= 0 || block_k <= 0) return 0;
-    const int64_t T = cdiv(max_seqlen, block_q);
-    const int64_t J = cdiv(max_seqlen, block_k);
+int64_t bsp_skip_bitmap_words_kv(int n_heads_q, int n_seqs, int max_seqlen_q, int max_seqlen_k, int block_q,
+                                 int block_k) {
+    if (n_heads_q <= 0 || n_seqs < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || block_q <= 0 || block_k <= 0)
+        return 0;
+    const int64_t T = cdiv(max_seqlen_q, block_q);
+    const int64_t J = cdiv(max_seqlen_k, block_k);
     const int64_t W = cdiv(J, 32);
     return (int64_t)n_heads_q * n_seqs * T * W;
+}
+
+int64_t bsp_skip_bitmap_words(int n_heads_q, int n_seqs, int max_seqlen, int block_q, int block_k) {
+    return bsp_skip_bitmap_words_kv(n_heads_q, n_seqs, max_seqlen, max_seqlen, block_q, block_k);
 }
 
 bsp_status_t bsp_attn_fwd(const bsp_tensor_t *q, const bsp_tensor_t *k, const bsp_tensor_t *v, bsp_tensor_t *o,
                           float *lse, const bsp_seqs_t *seqs, const bsp_block_table_t *bt, int n_heads_q,
                           int n_heads_kv, int head_dim, int block_q, int block_k, float lambda,
                           bsp_skip_out_t *skip_out, void *stream) {
+    return bsp_attn_fwd_ex(q, k, v, o, lse, seqs, bt, n_heads_q, n_heads_kv, head_dim, block_q, block_k, lambda,
+                           skip_out, stream, nullptr);
+}
+
+bsp_status_t bsp_attn_fwd_ex(const bsp_tensor_t *q, const bsp_tensor_t *k, const bsp_tensor_t *v, bsp_tensor_t *o,
+                             float *lse, const bsp_seqs_t *seqs, const bsp_block_table_t *bt, int n_heads_q,
+                             int n_heads_kv, int head_dim, int block_q, int block_k, float lambda,
+                             bsp_skip_out_t *skip_out, void *stream, const bsp_fwd_options_t *opts) {
     g_detail[0] = '\0';
+    bsp_fwd_options_t none;
+    memset(&none, 0, sizeof(none));
+    if (opts == nullptr) opts = &none;
+    if ((opts->flags & ~(BSP_FLAG_LOAD_SKIPPED_V | BSP_FLAG_EXP_SKIPPED)) != 0)
+        return fail(BSP_ERR_INVALID_ARG, "unknown option flags 0x%x", opts->flags);
+    const bool chunked = opts->cu_seqlens_k != nullptr;
+    if (chunked && (opts->max_seqlen_k < 0 || ((uintptr_t)opts->cu_seqlens_k & 3u) != 0))
+        return fail(BSP_ERR_INVALID_ARG, "cu_seqlens_k needs max_seqlen_k >= 0 and 4-byte alignment");
+    if (opts->lambda_per_seq != nullptr && ((uintptr_t)opts->lambda_per_seq & 3u) != 0)
+        return fail(BSP_ERR_INVALID_ARG, "lambda_per_seq not 4-byte aligned");
+    if (((uintptr_t)opts->skip_count_per_seq & 7u) != 0 || ((uintptr_t)opts->visited_count_per_seq & 7u) != 0)
+        return fail(BSP_ERR_INVALID_ARG, "per-sequence counts not 8-byte aligned");
     // ---------------- argument checks (host only, before any HIP call)
     if (n_heads_q <= 0 || n_heads_kv <= 0 || n_heads_q % n_heads_kv != 0)
         return fail(BSP_ERR_INVALID_ARG, "n_heads_q (%d) must be a positive multiple of n_heads_kv (%d)", n_heads_q,
@@ -1076,14 +1152,15 @@ bsp_status_t bsp_attn_fwd(const bsp_tensor_t *q, const bsp_tensor_t *k, const bs
         if (block_k % ps != 0 && ps % block_k != 0)
             return fail(BSP_ERR_INVALID_ARG, "block_k (%d) and page_size (%d) must divide one another", block_k, ps);
         while ((1 << page_shift) < ps) ++page_shift;
-        if ((int64_t)bt->max_pages_per_seq * ps < seqs->max_seqlen)
-            return fail(BSP_ERR_INVALID_ARG, "max_pages_per_seq * page_size < max_seqlen");
     }
+    const int max_k = chunked ? opts->max_seqlen_k : seqs->max_seqlen;  // key positions per sequence
+    if (paged && (int64_t)bt->max_pages_per_seq * bt->page_size < max_k)
+        return fail(BSP_ERR_INVALID_ARG, "max_pages_per_seq * page_size < max_seqlen%s", chunked ? "_k" : "");
     const int64_t T_max = cdiv(seqs->max_seqlen, block_q);
-    const int64_t J_max = cdiv(seqs->max_seqlen, block_k);
+    const int64_t J_max = cdiv(max_k, block_k);
     const int64_t W = cdiv(J_max, 32);
     uint32_t *bitmap = skip_out ? skip_out->bitmap : nullptr;
-    const int64_t words = bsp_skip_bitmap_words(n_heads_q, seqs->n_seqs, seqs->max_seqlen, block_q, block_k);
+    const int64_t words = bsp_skip_bitmap_words_kv(n_heads_q, seqs->n_seqs, seqs->max_seqlen, max_k, block_q, block_k);
     if (bitmap != nullptr) {
         if (((uintptr_t)bitmap & 3u) != 0) return fail(BSP_ERR_INVALID_ARG, "bitmap not 4-byte aligned");
         if (skip_out->bitmap_words < words)
@@ -1100,7 +1177,9 @@ bsp_status_t bsp_attn_fwd(const bsp_tensor_t *q, const bsp_tensor_t *k, const bs
     const int hpw = heads_per_workgroup(q->dtype, n_heads_q / n_heads_kv);
     const int64_t grid64 = T_max * (int64_t)seqs->n_seqs * (n_heads_q / hpw);
     if (grid64 > 0x7fffffffLL) return fail(BSP_ERR_INVALID_ARG, "too many work items");
-    kernel_fn fn = find_kernel(q->dtype, head_dim, block_q, block_k, paged, hpw, isinf(lambda));
+    // dense-mode kernel: lambda = +inf for every sequence (no vote, nothing to ablate)
+    const bool dense = isinf(lambda) && opts->lambda_per_seq == nullptr;
+    kernel_fn fn = find_kernel(q->dtype, head_dim, block_q, block_k, paged, hpw, dense);
     if (fn == nullptr)
         return fail(BSP_ERR_UNSUPPORTED, "no kernel for dtype %d, head_dim %d, block_q %d, block_k %d", (int)q->dtype,
                     head_dim, block_q, block_k);
@@ -1110,11 +1189,14 @@ bsp_status_t bsp_attn_fwd(const bsp_tensor_t *q, const bsp_tensor_t *k, const bs
     hipStream_t hs = (hipStream_t)stream;
     unsigned long long *c0 = skip_out ? skip_out->skip_count : nullptr;
     unsigned long long *c1 = skip_out ? skip_out->visited_count : nullptr;
-    if (bitmap != nullptr || c0 != nullptr || c1 != nullptr) {
-        const int64_t work = words > n_heads_q ? words : n_heads_q;
+    unsigned long long *c2 = opts->skip_count_per_seq;
+    unsigned long long *c3 = opts->visited_count_per_seq;
+    if (bitmap != nullptr || c0 != nullptr || c1 != nullptr || c2 != nullptr || c3 != nullptr) {
+        int64_t work = words > n_heads_q ? words : n_heads_q;
+        if (work < seqs->n_seqs) work = seqs->n_seqs;
         const int blocks = (int)(cdiv(work, 256) < 1024 ? cdiv(work, 256) : 1024);
         hipLaunchKernelGGL(fill_outputs, dim3(blocks > 0 ? blocks : 1), dim3(256), 0, hs, bitmap, words, c0, c1,
-                           n_heads_q);
+                           n_heads_q, c2, c3, seqs->n_seqs);
     }
     if (grid64 > 0) {
         FwdParams p;
@@ -1156,6 +1238,11 @@ bsp_status_t bsp_attn_fwd(const bsp_tensor_t *q, const bsp_tensor_t *k, const bs
         p.v_scale = v->scale;
         p.scale = (float)scale;
         p.lam = lambda;
+        p.cu_k = opts->cu_seqlens_k;
+        p.lam_seq = opts->lambda_per_seq;
+        p.seq_skip = c2;
+        p.seq_visited = c3;
+        p.flags = opts->flags;
         hipLaunchKernelGGL(fn, dim3((unsigned)grid64), dim3(block_q * 2 * hpw), 0, hs, p);
     }
     const hipError_t e = hipGetLastError();

@@ -138,6 +138,61 @@ bsp_status_t bsp_attn_fwd(const bsp_tensor_t *q, const bsp_tensor_t *k, const bs
 /* Number of uint32 words the skip bitmap needs (0 for invalid arguments). */
 int64_t bsp_skip_bitmap_words(int n_heads_q, int n_seqs, int max_seqlen, int block_q, int block_k);
 
+/*
+ * Options of bsp_attn_fwd_ex. Zero-initialise the struct and set what is
+ * needed; a NULL options pointer (or an all-zero struct) is bsp_attn_fwd.
+ *
+ *   - chunked prefill against a cached prefix (the guide's section 3.1: long
+ *     prompts are prefilled in chunks): with cu_seqlens_k set, sequence s has
+ *     Lq = cu_seqlens[s+1]-cu_seqlens[s] query rows (rows of q and o) and
+ *     Lk = cu_seqlens_k[s+1]-cu_seqlens_k[s] >= Lq keys/values (rows of k and
+ *     v, or positions of its block-table pages). The queries are the last Lq
+ *     positions: query row r sees keys 0 .. (Lk - Lq) + r (bottom-right causal
+ *     alignment). Lq = 1 is one decoding step. Lk < Lq is a caller error with
+ *     undefined results (the bounds live in device memory and are not read
+ *     on the host).
+ *   - a lambda per sequence (the guide's per-request threshold, sections 3.3
+ *     and 9.3): lambda_per_seq[s] >= 0 or +inf replaces the scalar lambda for
+ *     sequence s (negative or NaN values: undefined results). Calls with
+ *     lambda_per_seq always run the skip-deciding kernel.
+ *   - per-sequence counts (section 3.5: per-request sparsity): skip and
+ *     visited (tile, block) pairs summed over the query heads, uint64[n_seqs].
+ *   - ablation switches (the guide's skip_value_load / skip_softmax_exp
+ *     settings, section 5, step 3): BSP_FLAG_LOAD_SKIPPED_V copies V also for
+ *     blocks that every query head of the workgroup skips; BSP_FLAG_EXP_SKIPPED
+ *     computes (and discards) the exponentials of skipped blocks. Results are
+ *     unchanged; only the work done changes.
+ */
+#define BSP_FLAG_LOAD_SKIPPED_V 1u
+#define BSP_FLAG_EXP_SKIPPED 2u
+
+typedef struct {
+    const int32_t *cu_seqlens_k;   /* device int32[n_seqs+1] or NULL (= cu_seqlens) */
+    int32_t max_seqlen_k;          /* host: max Lk; required when cu_seqlens_k != NULL */
+    const float *lambda_per_seq;   /* device float[n_seqs] or NULL */
+    unsigned long long *skip_count_per_seq;     /* device uint64[n_seqs] or NULL */
+    unsigned long long *visited_count_per_seq;  /* device uint64[n_seqs] or NULL */
+    uint32_t flags;                /* BSP_FLAG_* */
+} bsp_fwd_options_t;
+
+/*
+ * bsp_attn_fwd_ex -- bsp_attn_fwd with the options above. Arguments as for
+ * bsp_attn_fwd; with cu_seqlens_k set, the bitmap rows are
+ * bsp_skip_bitmap_words_kv(...) long (one bit per key block up to
+ * max_seqlen_k) and paged caches need max_pages_per_seq * page_size >=
+ * max_seqlen_k. Unknown flag bits: BSP_ERR_INVALID_ARG.
+ */
+bsp_status_t bsp_attn_fwd_ex(const bsp_tensor_t *q, const bsp_tensor_t *k, const bsp_tensor_t *v,
+                             bsp_tensor_t *o, float *lse,
+                             const bsp_seqs_t *cu_seqlens, const bsp_block_table_t *block_table,
+                             int n_heads_q, int n_heads_kv, int head_dim, int block_q, int block_k,
+                             float lambda, bsp_skip_out_t *skip_mask_out, void *stream,
+                             const bsp_fwd_options_t *options);
+
+/* Bitmap words for a call with max_seqlen_k keys per sequence (0 for invalid arguments). */
+int64_t bsp_skip_bitmap_words_kv(int n_heads_q, int n_seqs, int max_seqlen_q, int max_seqlen_k, int block_q,
+                                 int block_k);
+
 /* Static text for a status code. */
 const char *bsp_status_string(int status);
 

@@ -65,21 +65,49 @@ def to_device(inp: synth.Inputs, device="cuda"):
     return d
 
 
-def run_gpu(inp: synth.Inputs, dev: Dict, block_q: int, block_k: int, lam: float, paged: bool = False):
+@dataclass
+class Chunk:
+    """Chunked prefill: sequence s's queries are its last lq[s] positions."""
+    lq: Sequence[int]
+
+    def rows(self, inp: synth.Inputs) -> np.ndarray:
+        cu = inp.cu_seqlens
+        return np.concatenate([np.arange(int(cu[s + 1]) - n, int(cu[s + 1])) for s, n in enumerate(self.lq)]
+                              + [np.zeros(0, int)]).astype(np.int64)
+
+    def cu_q(self) -> np.ndarray:
+        return np.concatenate([[0], np.cumsum(self.lq)]).astype(np.int32)
+
+
+def run_gpu(inp: synth.Inputs, dev: Dict, block_q: int, block_k: int, lam: float, paged: bool = False,
+            chunk: Optional[Chunk] = None, lam_seq: Optional[Sequence[float]] = None, flags: int = 0):
     import torch
 
     import block_sparse_long_bsp_amd as bsp
 
     k = dev["k_pages"] if paged else dev["k"]
     v = dev["v_pages"] if paged else dev["v"]
-    out = bsp.fwd(dev["q"], k, v, dev["cu"], inp.max_seqlen, block_table=dev.get("table") if paged else None,
+    n_seqs = len(inp.seqlens)
+    kw = {}
+    q, cu, max_q = dev["q"], dev["cu"], inp.max_seqlen
+    if chunk is not None:
+        q = dev["q"][torch.from_numpy(chunk.rows(inp)).to(q.device)].contiguous()
+        cu = torch.from_numpy(chunk.cu_q()).to(q.device)
+        max_q = max(list(chunk.lq) + [0])
+        kw.update(cu_seqlens_k=dev["cu"], max_seqlen_k=inp.max_seqlen)
+    if lam_seq is not None:
+        kw["lam_per_seq"] = torch.tensor(list(lam_seq), dtype=torch.float32, device=q.device)
+    seq_sc = torch.empty(n_seqs, dtype=torch.int64, device=q.device)
+    seq_vc = torch.empty(n_seqs, dtype=torch.int64, device=q.device)
+    out = bsp.fwd(q, k, v, cu, max_q, block_table=dev.get("table") if paged else None,
                   block_q=block_q, block_k=block_k, lam=lam, q_scale=dev["q_scale"], k_scale=dev["k_scale"],
-                  v_scale=dev["v_scale"])
+                  v_scale=dev["v_scale"], seq_skip_count=seq_sc, seq_visited_count=seq_vc, flags=flags, **kw)
     torch.cuda.synchronize()
     o, lse, bitmap, sc, vc = out
     return dict(o=o.float().cpu().numpy(), lse=lse.cpu().numpy(),
-                bits=bsp.unpack_bitmap(bitmap, inp.q.shape[1], len(inp.seqlens), inp.max_seqlen, block_q, block_k),
-                skip_count=sc.cpu().numpy(), visited_count=vc.cpu().numpy())
+                bits=bsp.unpack_bitmap(bitmap, inp.q.shape[1], n_seqs, max_q, block_q, block_k, inp.max_seqlen),
+                skip_count=sc.cpu().numpy(), visited_count=vc.cpu().numpy(),
+                seq_skip_count=seq_sc.cpu().numpy(), seq_visited_count=seq_vc.cpu().numpy())
 
 
 @dataclass
@@ -98,12 +126,31 @@ class Report:
 
 
 def compare(inp: synth.Inputs, gpu: Dict, block_q: int, block_k: int, lam: float,
-            work: Optional[np.ndarray] = None, n_threads: int = 0, check_counts: bool = True) -> Report:
+            work: Optional[np.ndarray] = None, n_threads: int = 0, check_counts: bool = True,
+            chunk: Optional[Chunk] = None, lam_seq: Optional[Sequence[float]] = None) -> Report:
     """Steps 2-6 of the protocol for the given work items (default: all)."""
     Hq = inp.q.shape[1]
     n_seqs = len(inp.seqlens)
     J = max(1, (inp.max_seqlen + block_k - 1) // block_k)
-    ref = oracle.run_inputs(inp, block_q, block_k, lam, work=work, n_threads=n_threads, j_max=J)
+    if chunk is None:
+        cu = inp.cu_seqlens
+        lq = list(inp.seqlens)
+
+        def run_ref(**kw):
+            return oracle.run_inputs(inp, block_q, block_k, lam, n_threads=n_threads, j_max=J, lam_seq=lam_seq, **kw)
+    else:
+        cu = chunk.cu_q()
+        lq = list(chunk.lq)
+        qrows = inp.q[chunk.rows(inp)]
+
+        def run_ref(**kw):
+            return oracle.run(qrows, inp.k, inp.v, cu, Hq, inp.k.shape[1], block_q, block_k, lam,
+                              q_scale=inp.q_scale, k_scale=inp.k_scale, v_scale=inp.v_scale, n_threads=n_threads,
+                              j_max=J, cu_seqlens_k=inp.cu_seqlens, lam_seq=lam_seq, **kw)
+    if work is None and chunk is not None:
+        work = synth.work_items(lq, Hq, block_q)
+    ref = run_ref(work=work)
+    lam_of = (lambda s_: lam) if lam_seq is None else (lambda s_: lam_seq[s_])
     rep = Report(n_items=ref.work.shape[0])
     gbits = np.zeros_like(ref.skip)
     for w, (s, h, t) in enumerate(ref.work):
@@ -115,7 +162,9 @@ def compare(inp: synth.Inputs, gpu: Dict, block_q: int, block_k: int, lam: float
         rep.problems.append("GPU bitmap has bits on unvisited pairs")
     diff = (gbits != ref.skip) & vis
     if diff.any():
-        margin = np.abs(ref.mingap - lam)
+        lam_item = np.array([lam_of(int(s_)) for s_ in ref.work[:, 0]])[:, None]
+        with np.errstate(invalid="ignore"):
+            margin = np.abs(ref.mingap - lam_item)
         hard = diff & ~(margin <= MARGIN_BAND[inp.dtype])
         if hard.any():
             idx = np.argwhere(hard)[:5]
@@ -124,10 +173,8 @@ def compare(inp: synth.Inputs, gpu: Dict, block_q: int, block_k: int, lam: float
                                             for i, j in idx))
         rep.n_band_flips = int(diff.sum())
         forced = np.where(vis, gbits, 0).astype(np.uint8)
-        ref = oracle.run_inputs(inp, block_q, block_k, lam, work=ref.work, forced=forced, n_threads=n_threads,
-                                j_max=J)
+        ref = run_ref(work=ref.work, forced=forced)
     rep.n_skipped = int((ref.skip.astype(bool) & vis).sum())
-    cu = inp.cu_seqlens
     tol = TOL[inp.dtype]
     errs = []
     lse_err = 0.0
@@ -159,24 +206,34 @@ def compare(inp: synth.Inputs, gpu: Dict, block_q: int, block_k: int, lam: float
         pop = bits.reshape(Hq, -1).sum(axis=1)
         if not np.array_equal(pop, gpu["skip_count"].astype(np.int64)):
             rep.problems.append(f"skip_count {gpu['skip_count'][:4]}... != bitmap popcount {pop[:4]}...")
-        vis_expect = np.zeros(Hq, dtype=np.int64)
-        for s, L in enumerate(inp.seqlens):
+        vis_expect = 0
+        vis_seq = np.zeros(n_seqs, dtype=np.int64)
+        for s, L in enumerate(lq):
+            off = int(inp.seqlens[s]) - L
             for t in range((L + block_q - 1) // block_q):
                 r1 = min(L, (t + 1) * block_q)
-                vis_expect += (r1 - 1) // block_k + 1
+                vis_seq[s] += ((off + r1 - 1) // block_k + 1) * Hq
+        vis_expect = np.full(Hq, vis_seq.sum() // max(Hq, 1), dtype=np.int64)
         if not np.array_equal(vis_expect, gpu["visited_count"].astype(np.int64)):
             rep.problems.append(f"visited_count {gpu['visited_count'][:4]} != {vis_expect[:4]}")
+        if "seq_skip_count" in gpu:
+            pop_seq = bits.transpose(1, 0, 2, 3).reshape(n_seqs, -1).sum(axis=1)
+            if not np.array_equal(pop_seq, gpu["seq_skip_count"].astype(np.int64)):
+                rep.problems.append(f"per-sequence skip counts {gpu['seq_skip_count'][:4]} != {pop_seq[:4]}")
+            if not np.array_equal(vis_seq, gpu["seq_visited_count"].astype(np.int64)):
+                rep.problems.append(f"per-sequence visited counts {gpu['seq_visited_count'][:4]} != {vis_seq[:4]}")
     return rep
 
 
 def check_case(inp: synth.Inputs, block_q: int, block_k: int, lams: Sequence[float], paged: bool = False,
-               work: Optional[np.ndarray] = None, dev=None) -> List[Report]:
+               work: Optional[np.ndarray] = None, dev=None, chunk: Optional[Chunk] = None,
+               lam_seq: Optional[Sequence[float]] = None, flags: int = 0) -> List[Report]:
     """Run the GPU for each lambda and compare; raise AssertionError on any problem."""
     dev = dev or to_device(inp)
     reps = []
     for lam in lams:
-        gpu = run_gpu(inp, dev, block_q, block_k, lam, paged=paged)
-        rep = compare(inp, gpu, block_q, block_k, lam, work=work)
+        gpu = run_gpu(inp, dev, block_q, block_k, lam, paged=paged, chunk=chunk, lam_seq=lam_seq, flags=flags)
+        rep = compare(inp, gpu, block_q, block_k, lam, work=work, chunk=chunk, lam_seq=lam_seq)
         reps.append(rep)
         assert rep.ok(), f"lambda={lam}: " + "; ".join(rep.problems)
     return reps

@@ -70,6 +70,9 @@ int main(void) {
          offsetof(bsp_seqs_t, total_tokens), sizeof(bsp_block_table_t), offsetof(bsp_block_table_t, page_size));
   printf("%zu %zu %zu %zu %zu %zu\n", sizeof(bsp_skip_out_t), offsetof(bsp_skip_out_t, bitmap_words),
          offsetof(bsp_skip_out_t, skip_count), offsetof(bsp_skip_out_t, visited_count), (size_t)0, (size_t)0);
+  printf("%zu %zu %zu %zu %zu %zu\n", sizeof(bsp_fwd_options_t), offsetof(bsp_fwd_options_t, max_seqlen_k),
+         offsetof(bsp_fwd_options_t, lambda_per_seq), offsetof(bsp_fwd_options_t, skip_count_per_seq),
+         offsetof(bsp_fwd_options_t, visited_count_per_seq), offsetof(bsp_fwd_options_t, flags));
   return 0;
 }
 '''
@@ -85,6 +88,9 @@ int main(void) {
                        ctypes.sizeof(BlockTable), BlockTable.page_size.offset]
     assert vals[2][:4] == [ctypes.sizeof(SkipOut), SkipOut.bitmap_words.offset, SkipOut.skip_count.offset,
                            SkipOut.visited_count.offset]
+    O = bsp.Options
+    assert vals[3] == [ctypes.sizeof(O), O.max_seqlen_k.offset, O.lambda_per_seq.offset, O.skip_count_per_seq.offset,
+                       O.visited_count_per_seq.offset, O.flags.offset]
 
 
 def test_bitmap_words_formula(lib):
@@ -161,6 +167,37 @@ def test_fp8_requires_scales(lib):
     kv = lambda: Tensor(FAKE, bsp.BSP_FP8_E4M3, 1024, 128, None)
     st = _call(q=t(), k=kv(), v=kv())
     assert st == bsp.BSP_ERR_INVALID_ARG
+
+
+def test_bitmap_words_with_separate_key_lengths(lib):
+    # rows per (head, seq, query tile); words per row from the key length
+    assert bsp.skip_bitmap_words_kv(32, 2, 1, 4096, 64, 64) == 32 * 2 * 1 * 2
+    assert bsp.skip_bitmap_words_kv(4, 1, 300, 300, 128, 64) == bsp.skip_bitmap_words(4, 1, 300, 128, 64)
+    assert bsp.skip_bitmap_words_kv(4, 1, 10, -1, 64, 64) == 0
+
+
+def _call_ex(opts, **over):
+    D, Hq, Hkv = 128, 32, 8
+    q = Tensor(FAKE, bsp.BSP_BF16, Hq * D, D, None)
+    kv = Tensor(FAKE, bsp.BSP_BF16, Hkv * D, D, None)
+    o = Tensor(FAKE, bsp.BSP_BF16, Hq * D, D, None)
+    seqs = Seqs(FAKE, 1, 256, 256)
+    so = over.pop("so", SkipOut(FAKE, bsp.skip_bitmap_words(Hq, 1, 256, 128, 128), FAKE, FAKE))
+    return bsp.fwd_raw(q, kv, kv, o, FAKE, seqs, over.pop("bt", None), Hq, Hkv, D, 128, 128, 2.0, so, 0, opts)
+
+
+@pytest.mark.parametrize("opts,expect", [
+    (bsp.Options(None, 0, None, None, None, 4), bsp.BSP_ERR_INVALID_ARG),            # unknown flag bit
+    (bsp.Options(FAKE, -1, None, None, None, 0), bsp.BSP_ERR_INVALID_ARG),           # negative max_seqlen_k
+    (bsp.Options(FAKE + 2, 512, None, None, None, 0), bsp.BSP_ERR_INVALID_ARG),      # misaligned cu_seqlens_k
+    (bsp.Options(None, 0, FAKE + 1, None, None, 0), bsp.BSP_ERR_INVALID_ARG),        # misaligned lambda array
+    (bsp.Options(None, 0, None, FAKE + 4, None, 0), bsp.BSP_ERR_INVALID_ARG),        # misaligned counts
+    (bsp.Options(FAKE, 8192, None, None, None, 0), bsp.BSP_ERR_INVALID_ARG),         # bitmap sized for 256 keys
+])
+def test_extended_options_rejected_before_the_device(lib, opts, expect):
+    st = _call_ex(opts)
+    assert st == expect, (st, bsp.last_error_detail())
+    assert bsp.last_error_detail() != ""
 
 
 def test_fp8_head_dim_64_is_unsupported(lib):

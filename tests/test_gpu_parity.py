@@ -128,6 +128,105 @@ def test_llama8b_128k_fp8_sampled():
     _sampled("llama8b_128k", heads=[0, 21], tile_stride=211, dtype="fp8")
 
 
+# ---- chunked prefill against a cached prefix (queries = the last Lq positions) --
+
+CHUNK_SEQS = (300, 129, 77, 513, 40)
+
+
+@pytest.mark.parametrize("dtype,inst", [("bf16", (128, 128, 128)), ("bf16", (128, 128, 64)), ("bf16", (64, 64, 64)),
+                                        ("fp8", (128, 128, 128)), ("f32", (64, 64, 64))],
+                         ids=lambda x: x if isinstance(x, str) else "d%d_q%d_k%d" % x)
+@pytest.mark.parametrize("paged", [False, True], ids=["packed", "paged"])
+def test_chunked_prefill(dtype, inst, paged):
+    D, bq, bk = inst
+    inp = synth.build_inputs(CHUNK_SEQS, 4, 2, D, dtype, rho=0.95, n_vert=2, code=210, paged=paged, page_size=64,
+                             sink_gain=6.0)
+    chunk = parity.Chunk(lq=(45, 129, 1, 200, 0))
+    _log(f"chunked prefill dtype={dtype} D={D} bq={bq} bk={bk} paged={paged}")
+    reps = parity.check_case(inp, bq, bk, [math.inf, 2.0, 0.0], paged=paged, chunk=chunk)
+    assert reps[0].n_skipped == 0 and reps[2].n_skipped > 0
+
+
+@pytest.mark.parametrize("paged", [False, True], ids=["packed", "paged"])
+def test_decode_step_is_a_chunk_of_one(paged):
+    # one new token per sequence against its whole context
+    seqs = (1, 64, 65, 700, 2049, 333)
+    inp = synth.build_inputs(seqs, 8, 2, 128, "bf16", rho=0.97, n_vert=4, code=211, paged=paged, page_size=64,
+                             sink_gain=6.0)
+    _log(f"decode step paged={paged}")
+    reps = parity.check_case(inp, 64, 64, [math.inf, 3.0, 1.0], paged=paged, chunk=parity.Chunk(lq=(1,) * len(seqs)))
+    assert reps[2].n_skipped > 0
+
+
+def test_chunk_after_whole_tiles_equals_rows_of_full_prefill():
+    # same tiles, same blocks, same decisions: the chunk's outputs equal the full
+    # prefill's rows bit for bit
+    import torch
+
+    import block_sparse_long_bsp_amd as bsp
+
+    L, P = 700, 256
+    inp = synth.build_inputs((L,), 8, 2, 128, "bf16", rho=0.97, n_vert=3, code=212, sink_gain=6.0)
+    dev = parity.to_device(inp)
+    for lam in (math.inf, 2.0):
+        o, lse, bm, sc, vc = bsp.fwd(dev["q"], dev["k"], dev["v"], dev["cu"], L, block_q=128, block_k=128, lam=lam)
+        cuq = torch.tensor([0, L - P], dtype=torch.int32, device="cuda")
+        o2, lse2, bm2, _, _ = bsp.fwd(dev["q"][P:].contiguous(), dev["k"], dev["v"], cuq, L - P, block_q=128,
+                                      block_k=128, lam=lam, cu_seqlens_k=dev["cu"], max_seqlen_k=L)
+        torch.cuda.synchronize()
+        assert torch.equal(o[P:], o2)
+        assert torch.equal(lse[:, P:], lse2)
+        b1 = bsp.unpack_bitmap(bm, 8, 1, L, 128, 128)
+        b2 = bsp.unpack_bitmap(bm2, 8, 1, L - P, 128, 128, L)
+        assert np.array_equal(b1[:, :, P // 128:], b2)
+
+
+def test_chunk8k_of_llama8b_32k_sampled():
+    # the last 8K-token chunk of the 32K layer against its 24K-token cached prefix
+    w = synth.WORKLOADS["llama8b_32k_bf16"]
+    inp = synth.make_workload(w.name)
+    chunk = parity.Chunk(lq=(8192,))
+    work = synth.work_items([8192], w.n_heads_q, w.block_q, heads=[3, 28], tile_stride=13)
+    _log(f"chunk 8K of 32K: {work.shape[0]} sampled work items")
+    reps = parity.check_case(inp, w.block_q, w.block_k, list(w.lambdas), work=work, chunk=chunk)
+    for lam, r in zip(w.lambdas, reps):
+        _log(f"  lambda={lam}: skipped {r.n_skipped}/{r.n_pairs} max-abs {r.max_abs:.3g}")
+
+
+# ---- lambda per sequence, counts per sequence, ablation switches --
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8", "f32"])
+def test_lambda_per_sequence(dtype):
+    D = 64 if dtype == "f32" else 128
+    seqs = (300, 129, 77, 513)
+    inp = synth.build_inputs(seqs, 4, 2, D, dtype, rho=0.95, n_vert=2, code=213, sink_gain=6.0)
+    bq, bk = (64, 64)
+    _log(f"lambda per sequence dtype={dtype}")
+    reps = parity.check_case(inp, bq, bk, [7.0], lam_seq=[0.0, math.inf, 2.0, 0.5])
+    assert reps[0].n_skipped > 0
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8", "f32"])
+def test_ablation_flags_leave_results_unchanged(dtype):
+    import torch
+
+    import block_sparse_long_bsp_amd as bsp
+
+    D = 64 if dtype == "f32" else 128
+    inp = synth.build_inputs((700, 129), 4, 2, D, dtype, rho=0.97, n_vert=2, code=214, sink_gain=6.0)
+    dev = parity.to_device(inp)
+    outs = []
+    for flags in (0, bsp.FLAG_LOAD_SKIPPED_V, bsp.FLAG_EXP_SKIPPED, bsp.FLAG_LOAD_SKIPPED_V | bsp.FLAG_EXP_SKIPPED):
+        r = bsp.fwd(dev["q"], dev["k"], dev["v"], dev["cu"], inp.max_seqlen, block_q=64, block_k=64, lam=1.0,
+                    q_scale=dev["q_scale"], k_scale=dev["k_scale"], v_scale=dev["v_scale"], flags=flags)
+        torch.cuda.synchronize()
+        outs.append([x.clone() for x in r])
+    assert int(outs[0][3].sum()) > 0
+    for x in outs[1:]:
+        for a, b in zip(outs[0], x):
+            assert torch.equal(a, b)
+
+
 def test_repeat_runs_are_bit_identical():
     import torch
 
