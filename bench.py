@@ -83,6 +83,27 @@ def time_calls(fn, steps, warmup):
     return start.elapsed_time(end) / steps  # ms per call
 
 
+def time_each(fn, steps, flush=None):
+    """Median of per-call event timings; with ``flush`` (a callable writing a
+    buffer larger than the last-level cache) run between calls, outside the
+    timed events."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    out = []
+    for _ in range(steps):
+        if flush is not None:
+            flush()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        b.synchronize()
+        out.append(a.elapsed_time(b))
+    return float(np.median(out))
+
+
 def cpu_baseline(inp, w, lam, target_s=15.0):
     """Time the CPU oracle on a bounded, deterministic sample of the workload
     and scale its rate to the whole job by visited (tile, block) pairs. The
@@ -141,6 +162,8 @@ def main():
     ap.add_argument("--workload", default="llama8b_32k_bf16")
     ap.add_argument("--dtype", default=None)
     ap.add_argument("--sparse-steps", type=int, default=10)
+    ap.add_argument("--extra-steps", type=int, default=10,
+                    help="calls per extra measurement (median/flushed timing, ablation, chunk, decode); 0 skips")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -273,6 +296,64 @@ def main():
             "speedup_vs_dense": ms / ms_l, "flop_model_speedup": 1.0 / (1.0 - f / 2.0),
         })
     result["sparse"] = sparse
+
+    # ---- per-call median, warm and with the last-level cache flushed between calls
+    if args.extra_steps > 0:
+        flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        result["timing"] = {
+            "mean_ms": ms,
+            "median_ms_warm": time_each(call(dense_lam), args.extra_steps),
+            "median_ms_flushed": time_each(call(dense_lam), args.extra_steps, flush=lambda: flush_buf.fill_(7)),
+            "flush": "512 MiB device fill between calls (MI355X last-level cache is 256 MiB)",
+        }
+        del flush_buf
+
+    # ---- ablation switches at the smallest finite lambda: what each saving is worth
+    finite = [x for x in lambdas if not math.isinf(x)]
+    if args.extra_steps > 0 and finite:
+        lam_a = min(finite)
+
+        def call_flags(fl):
+            return lambda: bsp.fwd(q, k, v, cu, inp.max_seqlen, block_table=table, block_q=w.block_q,
+                                   block_k=w.block_k, lam=lam_a, q_scale=scales[0], k_scale=scales[1],
+                                   v_scale=scales[2], out=o, lse=lse, bitmap=bm, skip_count=sc,
+                                   visited_count=vc, flags=fl)
+
+        ab = {}
+        for name, fl in (("skip_all", 0), ("load_skipped_v", bsp.FLAG_LOAD_SKIPPED_V),
+                         ("exp_skipped", bsp.FLAG_EXP_SKIPPED),
+                         ("load_v_and_exp_skipped", bsp.FLAG_LOAD_SKIPPED_V | bsp.FLAG_EXP_SKIPPED)):
+            ab[name] = time_calls(call_flags(fl), args.extra_steps, 2)
+        ab["skip_fraction"] = int(sc.sum().item()) / visited
+        result["ablation"] = {"lambda": lam_a, "ms": ab, "dense_ms": ms,
+                              "note": "flags keep the decisions and outputs; they only add back the V load "
+                                      "and/or the exps of skipped blocks"}
+
+    # ---- chunked prefill against a cached prefix and one decoding step (single-sequence workloads)
+    if args.extra_steps > 0 and len(inp.seqlens) == 1 and not w.paged and inp.seqlens[0] >= 16384:
+        L = inp.seqlens[0]
+        cu_k = torch.tensor([0, L], dtype=torch.int32, device="cuda")
+        rows = []
+        for lq in (8192, 1):
+            q_c = q[L - lq:].contiguous()
+            o_c = torch.empty((lq, H, D), dtype=o.dtype, device="cuda")
+            lse_c = torch.empty((H, lq), dtype=torch.float32, device="cuda")
+            cu_q = torch.tensor([0, lq], dtype=torch.int32, device="cuda")
+            for lam in [dense_lam] + finite[-1:]:
+                def fn(lam=lam):
+                    return bsp.fwd(q_c, k, v, cu_q, lq, block_q=w.block_q, block_k=w.block_k, lam=lam,
+                                   q_scale=scales[0], k_scale=scales[1], v_scale=scales[2], out=o_c,
+                                   lse=lse_c, want_bitmap=False, skip_count=sc, visited_count=vc,
+                                   cu_seqlens_k=cu_k, max_seqlen_k=L)
+                ms_c = time_calls(fn, args.extra_steps, 2)
+                vis, skp = int(vc.sum().item()), int(sc.sum().item())
+                kept_c = vis - skp
+                kv_bytes = (vis + kept_c) * w.block_k * D * k.element_size() * (w.n_heads_kv / H)
+                rows.append({"lq": lq, "lk": L, "lambda": lam, "ms": ms_c, "query_tokens_per_s": lq / (ms_c * 1e-3),
+                             "skip_fraction": skp / vis,
+                             "executed_tflops": unit_flops * (vis + kept_c) / (ms_c * 1e-3) / 1e12,
+                             "kv_gbs": kv_bytes / (ms_c * 1e-3) / 1e9 if lq == 1 else None})
+        result["chunked"] = rows
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, w, dense_lam, target_s=args.cpu_seconds)

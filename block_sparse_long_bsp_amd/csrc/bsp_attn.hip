@@ -202,6 +202,8 @@ __device__ __forceinline__ void log_decision(const FwdParams &p, SkipLog &lg, in
 // used by the skip decision is tracked exactly and separately.
 // ---------------------------------------------------------------------------
 constexpr float kRescaleLog2 = 8.0f;
+// LDS operand reads in flight ahead of the MFMA that uses them (dense ping-pong matrix phase).
+constexpr int kPingPongDepth = 6;
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -392,9 +394,15 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
                 lds_copy16(src + kv_row<PAGED>(p, s, kbase, kk, stb) + lci, dst + (i * NW + w) * 1024);
             }
         } else {
+            // row kk - kb0 = min(r, lim) with lim = min(Lk - 1 - kb0, BK - 1), as
+            // min(crow0, lim - i*CSTEP) * stride + i*CSTEP * stride: one vector min and
+            // one add per copy (the per-lane crow0 * stride is loop-invariant); every
+            // term is below BK * stride < 2^31.
             const int kb0 = min(kb, Lk - 1);
-            lds_copy16_sb(src + (int64_t)(kbase + kb0) * stb, (uint32_t)((kk - kb0) * stb) + (uint32_t)lci,
-                          dst + (i * NW + w) * 1024);
+            const int sb = (int)stb;
+            const int lim = min(Lk - 1 - kb0, BK - 1);
+            const int rowb = min(crow0 * sb, (lim - i * CSTEP) * sb) + i * CSTEP * sb + lci;
+            lds_copy16_sb(src + (int64_t)(kbase + kb0) * stb, (uint32_t)rowb, dst + (i * NW + w) * 1024);
         }
     };
     auto copy_block = [&](const char *src, int64_t stb, int kb, char *dst, bool swz) {
@@ -616,7 +624,152 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
         return rs0 + rs1;
     };
 
-    if constexpr (DENSE) {
+    // Ping-pong dense schedule: bf16, two query heads of four waves each, so
+    // that waves w and w + 4 (which share a SIMD) belong to different heads.
+    constexpr bool PP = DENSE && !F8 && HPW == 2 && WPH == 4;
+
+    if constexpr (PP) {
+        // ---- dense ping-pong. Per block j every wave runs a matrix phase
+        // M_j = PV_{j-1} + QK_j and a vector phase V_j (mask, max, reference,
+        // exponentials, row sum, bf16 probabilities). Head 1 runs half a block
+        // behind head 0, the two separated by workgroup barriers: while head 0
+        // runs M_j head 1 runs V_{j-1}, and while head 0 runs V_j head 1 runs
+        // M_j. Each SIMD then holds one wave in a matrix phase and one in a
+        // vector phase at all times, and its matrix cores and vector ALU work
+        // side by side instead of taking turns. Interval 2j is the one in
+        // which head 0 runs M_j; at its start every wave issues its share of
+        // the copies of K_{j+1} and V_j. Each wave waits for its copies at the
+        // end of interval 2j + 1, so they have two intervals to land, and they
+        // fill the buffers of K_{j-1} and V_{j-2}, whose last reader (head 1's
+        // M_{j-1}) ran in interval 2j - 1.
+        auto issue_copy = [&](int j, int i) {  // copy i of this wave's share (K first, then V)
+            if (i < CI) copy_one(kg, kstb, (j + 1) * BK, sK[(j + 1) & 1], true, i);
+            else copy_one(vg, vstb, j * BK, sV[j & 1], true, i - CI);
+        };
+        // M phase: PV_{j-1} (probabilities pprev, V_{j-1} in LDS) and then QK_j
+        // (K_j in LDS -> sacc). Only one wave of the SIMD issues matrix work in
+        // this interval, so the LDS operand of MFMA s is read PD MFMAs ahead to
+        // cover the read latency; running PV first and QK second keeps the
+        // score accumulators dead while pprev is live. When this wave issues
+        // the copies of the interval here, they go one every CSLOT MFMAs.
+        auto m_phase = [&](int j, auto do_pv, auto do_qk, auto do_copy) {
+            constexpr bool PV = decltype(do_pv)::value, QK = decltype(do_qk)::value;
+            constexpr bool CP = decltype(do_copy)::value;
+            constexpr int NQK = KS * MT;
+            constexpr int P0 = PV ? NPV : 0;       // first QK slot
+            constexpr int NS = P0 + (QK ? NQK : 0);
+            constexpr int PD = kPingPongDepth;
+            constexpr int CSLOT = NS / (2 * CI);
+            static_assert(!CP || NS % (2 * CI) == 0, "copies must spread evenly over the matrix phase");
+            const char *kbuf = sK[j & 1];
+            const char *vbuf = sV[(j - 1) & 1];
+            auto opread = [&](int x) -> bf16x8 {
+                if (x < P0) return vread_at(vbuf, x / DT, x % DT);
+                const int f = x - P0, ks = f / MT, mt = f % MT;
+                return *(const bf16x8 *)(kbuf + krow + 32 * mt * KROWB + (((2 * ks + hh) ^ ksw) << 4));
+            };
+            // This wave's MFMAs issue ahead of its SIMD partner's vector work.
+            __builtin_amdgcn_s_setprio(1);
+            bf16x8 op[NS];
+#pragma unroll
+            for (int x = 0; x < PD && x < NS; ++x) op[x] = opread(x);
+#pragma unroll
+            for (int x = 0; x < NS; ++x) {
+                if (x + PD < NS) op[x + PD] = opread(x + PD);
+                if (x < P0) {
+                    oacc[x % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[x], pprev[x / DT], oacc[x % DT], 0, 0, 0);
+                } else {
+                    const int f = x - P0;
+                    sacc[f % MT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[x], qf[f / MT],
+                                                                           f < MT ? f32x16{} : sacc[f % MT], 0, 0, 0);
+                }
+                if constexpr (CP) {
+                    if (x % CSLOT == 0) {
+                        SCHED_FENCE();
+                        issue_copy(j, x / CSLOT);
+                    }
+                }
+                SCHED_FENCE();
+            }
+            __builtin_amdgcn_s_setprio(0);
+        };
+        // V phase of block j; the copies of the interval (when this wave issues
+        // them here, for block cj) go one per group of exponentials.
+        auto v_phase = [&](int j, auto do_copy, int cj) {
+            constexpr bool CP = decltype(do_copy)::value;
+            constexpr int EG = NE / (2 * CI);  // exponentials per copy
+            const int kb = j * BK;
+            if (kb + BK - 1 > off + q0) {  // causal mask (only where the block reaches past this wave's first query)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int key = kb + 32 * mt + 8 * (i >> 2) + 4 * hh + (i & 3);
+                        if (key > qpos) sacc[mt][i] = -INFINITY;
+                    }
+            }
+            float m = -INFINITY;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) m = max_fold16(m, sacc[mt]);
+            m = fmaxf(m, __shfl_xor(m, 32));
+            float alpha;
+            bool resc;
+            const float mc = new_reference(m, alpha, resc);
+            float rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+            for (int e = 0; e < NE; ++e) {
+                pe[e] = __builtin_amdgcn_exp2f(fmaf(sacc[e >> 4][e & 15], c, -mc));
+                if (e & 1) {
+                    rs0 += pe[e - 1];
+                    rs1 += pe[e];
+                }
+                if constexpr (CP) {
+                    if (e % EG == EG - 1) {
+                        SCHED_FENCE();
+                        issue_copy(cj, e / EG);
+                        SCHED_FENCE();
+                    }
+                }
+            }
+            finish_block(rs0 + rs1, alpha, resc);
+        };
+        using T_ = std::true_type;
+        using F_ = std::false_type;
+        const int n = nblk;
+        if (hl == 0) {
+            m_phase(0, F_{}, T_{}, T_{});                 // interval 0
+            __syncthreads();
+            v_phase(0, F_{}, 0);                          // interval 1
+            wait_vmem_all();
+            __syncthreads();
+            for (int j = 1; j < n; ++j) {
+                m_phase(j, T_{}, T_{}, T_{});             // interval 2j
+                __syncthreads();
+                v_phase(j, F_{}, 0);                      // interval 2j + 1
+                wait_vmem_all();
+                __syncthreads();
+            }
+            m_phase(n, T_{}, F_{}, F_{});                 // interval 2n: PV_{n-1}
+        } else {
+#pragma unroll
+            for (int i = 0; i < 2 * CI; ++i) issue_copy(0, i);  // interval 0: K_1, V_0
+            __syncthreads();
+            m_phase(0, F_{}, T_{}, F_{});                 // interval 1
+            wait_vmem_all();
+            __syncthreads();
+            for (int j = 1; j < n; ++j) {
+                v_phase(j - 1, T_{}, j);                  // interval 2j (copies of K_{j+1}, V_j)
+                __syncthreads();
+                m_phase(j, T_{}, T_{}, F_{});             // interval 2j + 1
+                wait_vmem_all();
+                __syncthreads();
+            }
+            v_phase(n - 1, F_{}, 0);                      // interval 2n
+            m_phase(n, T_{}, F_{}, F_{});                 // interval 2n + 1: PV_{n-1}
+        }
+        pend = false;
+        v_prev = false;
+    } else if constexpr (DENSE) {
         // ---- dense mode: every block is kept. Block 0 has no pending PV; every
         // later block runs the PV product of the previous block interleaved with
         // its own exponentials and row sum: group g is PV MFMA g (V operand read
