@@ -27,8 +27,9 @@ LIB_PATH = os.environ.get("BSP_ATTN_LIB") or os.path.join(_PKG, "libbsp_attn.so"
 BSP_OK, BSP_ERR_INVALID_ARG, BSP_ERR_UNSUPPORTED, BSP_ERR_HIP, BSP_ERR_DEVICE = range(5)
 BSP_F32, BSP_BF16, BSP_FP8_E4M3 = 0, 1, 2
 
-EXPORTED = ("bsp_attn_fwd", "bsp_attn_fwd_ex", "bsp_skip_bitmap_words", "bsp_skip_bitmap_words_kv",
-            "bsp_status_string", "bsp_last_error_detail", "bsp_version")
+EXPORTED = ("bsp_attn_fwd", "bsp_attn_fwd_ex", "bsp_attn_decode", "bsp_decode_workspace_bytes",
+            "bsp_skip_bitmap_words", "bsp_skip_bitmap_words_kv", "bsp_status_string", "bsp_last_error_detail",
+            "bsp_version")
 
 # ablation switches of bsp_attn_fwd_ex (results unchanged, only the work done changes)
 FLAG_LOAD_SKIPPED_V = 1  # copy V also for blocks every query head of the workgroup skips
@@ -67,6 +68,11 @@ class Options(ctypes.Structure):
                 ("flags", ctypes.c_uint32)]
 
 
+class DecodeOptions(ctypes.Structure):
+    _fields_ = [("lambda_per_seq", ctypes.c_void_p), ("skip_count_per_seq", ctypes.c_void_p),
+                ("visited_count_per_seq", ctypes.c_void_p), ("flags", ctypes.c_uint32)]
+
+
 _lib = None
 
 
@@ -85,6 +91,12 @@ def load_library(path: str = LIB_PATH):
                                  ctypes.c_int, ctypes.c_float, P, P]
     lib.bsp_attn_fwd_ex.restype = ctypes.c_int
     lib.bsp_attn_fwd_ex.argtypes = lib.bsp_attn_fwd.argtypes + [P]
+    lib.bsp_attn_decode.restype = ctypes.c_int
+    lib.bsp_attn_decode.argtypes = [P, P, P, P, P, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_float, P, P, P, P, ctypes.c_int64]
+    lib.bsp_decode_workspace_bytes.restype = ctypes.c_int64
+    lib.bsp_decode_workspace_bytes.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
+                                               ctypes.c_int, ctypes.c_int]
     lib.bsp_skip_bitmap_words.restype = ctypes.c_int64
     lib.bsp_skip_bitmap_words.argtypes = [ctypes.c_int] * 5
     lib.bsp_skip_bitmap_words_kv.restype = ctypes.c_int64
@@ -223,6 +235,93 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Ten
                        seq_visited_count.data_ptr() if seq_visited_count is not None else None, int(flags))
     st = fwd_raw(_desc(q, q_scale), _desc(k3, k_scale), _desc(v3, v_scale), _desc(out), lse.data_ptr() if lse is not None else 0,
                  seqs, bt, Hq, Hkv, D, block_q, block_k, float(lam), so, stream, opts)
+    if st != BSP_OK:
+        raise BspError(st, last_error_detail())
+    return out, lse, bitmap, skip_count, visited_count
+
+
+def decode_workspace_bytes(n_heads_q: int, n_heads_kv: int, n_seqs: int, total_k: int, max_seqlen_k: int,
+                           head_dim: int, block_k: int) -> int:
+    return int(load_library().bsp_decode_workspace_bytes(n_heads_q, n_heads_kv, n_seqs, total_k, max_seqlen_k,
+                                                         head_dim, block_k))
+
+
+def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_k: torch.Tensor, max_seqlen_k: int, *,
+           total_k: Optional[int] = None, block_table: Optional[torch.Tensor] = None, block_k: int = 128,
+           lam: float = math.inf, q_scale: Optional[torch.Tensor] = None, k_scale: Optional[torch.Tensor] = None,
+           v_scale: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+           lse: Optional[torch.Tensor] = None, bitmap: Optional[torch.Tensor] = None,
+           skip_count: Optional[torch.Tensor] = None, visited_count: Optional[torch.Tensor] = None,
+           want_bitmap: bool = True, want_lse: bool = True, lam_per_seq: Optional[torch.Tensor] = None,
+           seq_skip_count: Optional[torch.Tensor] = None, seq_visited_count: Optional[torch.Tensor] = None,
+           flags: int = 0, workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, ...]:
+    """One decoding step (``bsp_attn_decode``) on the current stream.
+
+    q [n_seqs, Hq, D]: each sequence's new query row, which sees all of its
+    keys; k, v packed [total_k, Hkv, D] or paged [n_pages, page_size, Hkv, D]
+    with ``block_table``; cu_seqlens_k int32 [n_seqs+1] on the device (the
+    key counts include the new token). ``total_k`` is cu_seqlens_k[-1]
+    (rows of the score workspace; for packed K/V it defaults to k's rows).
+    Returns (o, lse, bitmap, skip_count, visited_count); the bitmap rows are
+    [Hq, n_seqs, 1, J] in the layout of ``unpack_bitmap``. ``workspace``
+    (uint8, at least ``decode_workspace_bytes`` bytes) may be passed in to
+    avoid an allocation.
+    """
+    load_library()
+    if q.device.type != "cuda":
+        raise ValueError("q must be a device tensor")
+    n_seqs, Hq, D = q.shape
+    paged = block_table is not None
+    if paged:
+        if k.dim() != 4:
+            raise ValueError("paged k/v must be [n_pages, page_size, Hkv, D]")
+        page_size = k.shape[1]
+        k3 = k.view(k.shape[0] * k.shape[1], k.shape[2], k.shape[3])
+        v3 = v.view(v.shape[0] * v.shape[1], v.shape[2], v.shape[3])
+        if total_k is None:
+            raise ValueError("paged decoding needs total_k (= cu_seqlens_k[-1])")
+    else:
+        k3, v3 = k, v
+        if total_k is None:
+            total_k = k.shape[0]
+    Hkv = k3.shape[1]
+    if out is None:
+        out = torch.empty((n_seqs, Hq, D), dtype=torch.bfloat16, device=q.device)
+    if want_lse and lse is None:
+        lse = torch.empty((Hq, n_seqs), dtype=torch.float32, device=q.device)
+    words = skip_bitmap_words_kv(Hq, n_seqs, 1, max_seqlen_k, 1, block_k) if n_seqs > 0 else 0
+    if want_bitmap and bitmap is None:
+        bitmap = torch.empty((max(words, 1),), dtype=torch.int32, device=q.device)
+    if skip_count is None:
+        skip_count = torch.empty((Hq,), dtype=torch.int64, device=q.device)
+    if visited_count is None:
+        visited_count = torch.empty((Hq,), dtype=torch.int64, device=q.device)
+    need = decode_workspace_bytes(Hq, Hkv, n_seqs, int(total_k), int(max_seqlen_k), D, block_k)
+    if need < 0:
+        raise ValueError("invalid decode sizes")
+    if workspace is None:
+        workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=q.device)
+    for name, x, dt in (("cu_seqlens_k", cu_seqlens_k, torch.int32), ("lam_per_seq", lam_per_seq, torch.float32),
+                        ("seq_skip_count", seq_skip_count, torch.int64),
+                        ("seq_visited_count", seq_visited_count, torch.int64)):
+        if x is not None and (x.dtype != dt or not x.is_contiguous() or x.device != q.device):
+            raise ValueError(f"{name} must be a contiguous {dt} tensor on {q.device}")
+    seqs = Seqs(cu_seqlens_k.data_ptr(), n_seqs, int(max_seqlen_k), int(total_k))
+    bt = BlockTable(block_table.data_ptr(), block_table.shape[1], page_size) if paged else None
+    so = SkipOut(bitmap.data_ptr() if bitmap is not None else None, bitmap.numel() if bitmap is not None else 0,
+                 skip_count.data_ptr(), visited_count.data_ptr())
+    opts = DecodeOptions(lam_per_seq.data_ptr() if lam_per_seq is not None else None,
+                         seq_skip_count.data_ptr() if seq_skip_count is not None else None,
+                         seq_visited_count.data_ptr() if seq_visited_count is not None else None, int(flags))
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    lib = load_library()
+    st = int(lib.bsp_attn_decode(ctypes.byref(_desc(q, q_scale)), ctypes.byref(_desc(k3, k_scale)),
+                                 ctypes.byref(_desc(v3, v_scale)), ctypes.byref(_desc(out)),
+                                 ctypes.c_void_p(lse.data_ptr() if lse is not None else None), ctypes.byref(seqs),
+                                 ctypes.byref(bt) if bt is not None else None, Hq, Hkv, D, block_k,
+                                 ctypes.c_float(float(lam)), ctypes.byref(so), ctypes.c_void_p(stream or None),
+                                 ctypes.byref(opts), ctypes.c_void_p(workspace.data_ptr()),
+                                 ctypes.c_int64(workspace.numel() * workspace.element_size())))
     if st != BSP_OK:
         raise BspError(st, last_error_detail())
     return out, lse, bitmap, skip_count, visited_count

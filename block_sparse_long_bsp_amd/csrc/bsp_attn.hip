@@ -1099,6 +1099,370 @@ __global__ void __launch_bounds__(BQ * 2) fwd_f32(FwdParams p) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Decoding step: one new query row per sequence against all of its keys
+// (the guide's decode-phase use of the same rule). The row's causal window is
+// every key, so the tile-wide rule reduces to one row: block j is skipped
+// when max(M_0 .. M_{j-1}) - M_j > lambda, with M_j the block's largest score.
+// That prefix maximum does not depend on earlier decisions (a skipped block
+// never holds a larger score), so the key range of a sequence splits into
+// chunks that decide independently and exactly:
+//   dec_scores:  S = q.k for every key (dequantised), block maxima M;
+//   dec_pv:      per chunk, the prefix max before the chunk and the
+//                sequence's overall max Mall (from M), the decisions, and
+//                sum p*v, sum p over kept blocks with p = exp(scale*(S - Mall));
+//   dec_combine: o = sum over chunks / sum of p, lse = scale*Mall + ln(sum p).
+// The kernels are bound by HBM bytes: K once, V for blocks some query head of
+// the KV group keeps, the scores written and read once. All vector ALU: four
+// query heads per KV head are too few rows for the matrix cores.
+// ---------------------------------------------------------------------------
+struct DecParams {
+    const void *q, *k, *v;
+    void *o;
+    float *lse;
+    int64_t q_st, q_sh, k_st, k_sh, v_st, v_sh, o_st, o_sh;  // elements; q and o rows are sequences
+    int64_t lse_sh;                // elements between heads of lse (= n_seqs)
+    int64_t total_k;               // score rows per head (= cu_k[n_seqs])
+    const int32_t *cu_k;           // key offsets per sequence (packed rows; score rows)
+    const int32_t *table;          // paged: block table, else NULL
+    int32_t max_pages, page_shift;
+    uint32_t *bitmap;
+    unsigned long long *skip_count, *visited_count, *seq_skip, *seq_visited;
+    int32_t n_seqs, W, J_max, n_chunks, C, BK, Hq, Hkv, G;
+    float c_log2, lam_raw, scale;  // lam_raw: lambda / scale (scores are unscaled dot products)
+    const float *lam_seq;
+    const float *q_scale, *k_scale, *v_scale;
+    uint32_t flags;
+    float *S;     // [Hq][total_k]
+    float *M;     // [Hq][n_seqs][J_max]
+    float *part;  // [Hq][n_seqs][n_chunks][D + 1]: sum p*v over the chunk, then sum p
+};
+
+// Sum over the LPR consecutive lanes that hold one K/V row (LPR = 8 or 16),
+// through DPP: quad exchanges (lane ^ 1, lane ^ 2), then the mirror within
+// each 8 lanes and, for 16, within each 16 lanes. Every lane gets the sum.
+template <int LPR>
+__device__ __forceinline__ float row_sum(float x) {
+    auto dpp = [](float v, int ctrl) -> float {
+        switch (ctrl) {
+            case 0: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
+            case 1: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));
+            case 2: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, true));
+            default: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x140, 0xF, 0xF, true));
+        }
+    };
+    x += dpp(x, 0);
+    x += dpp(x, 1);
+    x += dpp(x, 2);
+    if constexpr (LPR == 16) x += dpp(x, 3);
+    return x;
+}
+
+// 16 bytes of a row as fp32: 8 bf16 values, or 16 e4m3 codes (widened exactly).
+template <bool F8>
+__device__ __forceinline__ void widen16(const u32x4 x, float *f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if constexpr (F8) {
+            const uint32_t lo = fp8x2_to_bf16x2<false>(x[i]), hi = fp8x2_to_bf16x2<true>(x[i]);
+            f[4 * i + 0] = __builtin_bit_cast(float, lo << 16);
+            f[4 * i + 1] = __builtin_bit_cast(float, lo & 0xffff0000u);
+            f[4 * i + 2] = __builtin_bit_cast(float, hi << 16);
+            f[4 * i + 3] = __builtin_bit_cast(float, hi & 0xffff0000u);
+        } else {
+            f[2 * i + 0] = __builtin_bit_cast(float, x[i] << 16);
+            f[2 * i + 1] = __builtin_bit_cast(float, x[i] & 0xffff0000u);
+        }
+    }
+}
+
+// Byte address of key `key` of sequence s in K or V of KV head g (base already at head g).
+template <bool PAGED>
+__device__ __forceinline__ const char *dec_row(const DecParams &p, const char *base_g, int64_t stb, int s, int kbase,
+                                               int key) {
+    if constexpr (PAGED) {
+        const int pg = p.table[(int64_t)s * p.max_pages + min(key >> p.page_shift, p.max_pages - 1)];
+        return base_g + (((int64_t)pg << p.page_shift) + (key & ((1 << p.page_shift) - 1))) * stb;
+    } else {
+        return base_g + (int64_t)(kbase + key) * stb;
+    }
+}
+
+// Work item of the decode kernels: (sequence, KV head, chunk of C key blocks).
+__device__ __forceinline__ bool dec_item(const DecParams &p, int &s, int &g, int &c, int &kbase, int &Lk, int &nblk,
+                                         int &j0, int &j1) {
+    int item = blockIdx.x;
+    c = item % p.n_chunks;
+    item /= p.n_chunks;
+    g = item % p.Hkv;
+    s = item / p.Hkv;
+    kbase = p.cu_k[s];
+    Lk = p.cu_k[s + 1] - kbase;
+    nblk = Lk > 0 ? min((Lk + p.BK - 1) / p.BK, p.J_max) : 0;
+    j0 = c * p.C;
+    j1 = min(j0 + p.C, nblk);
+    return j0 < j1;
+}
+
+// Scores and block maxima. 4 waves; a row of K is read by LPR lanes, 16 bytes
+// each, and a wave covers RPW rows per load.
+template <int IN, int D, bool PAGED, int GP>
+__global__ void __launch_bounds__(256) dec_scores(DecParams p) {
+    constexpr bool F8 = IN == BSP_FP8_E4M3;
+    constexpr int ES = F8 ? 1 : 2;
+    constexpr int LPR = D * ES / 16;
+    constexpr int EPL = 16 / ES;
+    constexpr int RPW = 64 / LPR;
+    static_assert(LPR == 8 || LPR == 16, "a row is 8 or 16 lanes");
+    int s, g, c, kbase, Lk, nblk, j0, j1;
+    if (!dec_item(p, s, g, c, kbase, Lk, nblk, j0, j1)) return;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int sub = lane % LPR, rw = lane / LPR;
+    const int G = p.G;
+    float qv[GP][EPL];
+    float sqk[GP];
+#pragma unroll
+    for (int h = 0; h < GP; ++h) {
+        const int hq = g * G + (h < G ? h : 0);
+        const u32x4 x = *(const u32x4 *)((const char *)p.q + ((int64_t)s * p.q_st + (int64_t)hq * p.q_sh) * ES + 16 * sub);
+        widen16<F8>(x, qv[h]);
+        sqk[h] = F8 ? p.q_scale[hq] * p.k_scale[g] : 1.f;
+    }
+    const char *kg = (const char *)p.k + (int64_t)g * p.k_sh * ES;
+    const int64_t kst = p.k_st * ES;
+    __shared__ float smax[4][GP];
+    for (int j = j0; j < j1; ++j) {
+        const int kb = j * p.BK;
+        const int rows = min(p.BK, Lk - kb);
+        float bmax[GP];
+#pragma unroll
+        for (int h = 0; h < GP; ++h) bmax[h] = -INFINITY;
+        for (int r0 = w * RPW; r0 < rows; r0 += 4 * RPW) {
+            const int r = r0 + rw;
+            const bool ok = r < rows;
+            const int key = kb + (ok ? r : rows - 1);
+            const u32x4 x = *(const u32x4 *)(dec_row<PAGED>(p, kg, kst, s, kbase, key) + 16 * sub);
+            float kf[EPL];
+            widen16<F8>(x, kf);
+#pragma unroll
+            for (int h = 0; h < GP; ++h) {
+                float d = 0.f;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) d = fmaf(qv[h][e], kf[e], d);
+                d = row_sum<LPR>(d) * sqk[h];
+                if (ok) {
+                    bmax[h] = fmaxf(bmax[h], d);
+                    if (sub == h && h < G) p.S[(int64_t)(g * G + h) * p.total_k + kbase + kb + r] = d;
+                }
+            }
+        }
+        // block maxima: over the rows of this wave, then over the 4 waves
+#pragma unroll
+        for (int h = 0; h < GP; ++h) {
+#pragma unroll
+            for (int m = LPR; m < 64; m <<= 1) bmax[h] = fmaxf(bmax[h], __shfl_xor(bmax[h], m));
+        }
+        if (lane == 0) {
+#pragma unroll
+            for (int h = 0; h < GP; ++h) smax[w][h] = bmax[h];
+        }
+        __syncthreads();
+        if (tid < G && tid < GP) {
+            float m = smax[0][tid];
+#pragma unroll
+            for (int x = 1; x < 4; ++x) m = fmaxf(m, smax[x][tid]);
+            p.M[((int64_t)(g * G + tid) * p.n_seqs + s) * p.J_max + j] = m;
+        }
+        __syncthreads();
+    }
+}
+
+// Decisions, probabilities and the partial PV of one chunk.
+template <int IN, int D, bool PAGED, int GP>
+__global__ void __launch_bounds__(256) dec_pv(DecParams p) {
+    constexpr bool F8 = IN == BSP_FP8_E4M3;
+    constexpr int ES = F8 ? 1 : 2;
+    constexpr int LPR = D * ES / 16;
+    constexpr int EPL = 16 / ES;
+    constexpr int RPW = 64 / LPR;
+    int s, g, c, kbase, Lk, nblk, j0, j1;
+    if (!dec_item(p, s, g, c, kbase, Lk, nblk, j0, j1)) return;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int sub = lane % LPR, rw = lane / LPR;
+    const int G = p.G;
+    __shared__ float sred[4][GP][2];
+    __shared__ float sacc[4][GP][D + 1];
+
+    // overall max and the max before this chunk, per head, from the block maxima
+    float mall[GP], mpre[GP];
+#pragma unroll
+    for (int h = 0; h < GP; ++h) mall[h] = mpre[h] = -INFINITY;
+    for (int j = tid; j < nblk; j += 256) {
+#pragma unroll
+        for (int h = 0; h < GP; ++h) {
+            if (h < G) {
+                const float x = p.M[((int64_t)(g * G + h) * p.n_seqs + s) * p.J_max + j];
+                mall[h] = fmaxf(mall[h], x);
+                if (j < j0) mpre[h] = fmaxf(mpre[h], x);
+            }
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < GP; ++h)
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1) {
+            mall[h] = fmaxf(mall[h], __shfl_xor(mall[h], m));
+            mpre[h] = fmaxf(mpre[h], __shfl_xor(mpre[h], m));
+        }
+    if (lane == 0) {
+#pragma unroll
+        for (int h = 0; h < GP; ++h) {
+            sred[w][h][0] = mall[h];
+            sred[w][h][1] = mpre[h];
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < GP; ++h) {
+        mall[h] = fmaxf(fmaxf(sred[0][h][0], sred[1][h][0]), fmaxf(sred[2][h][0], sred[3][h][0]));
+        mpre[h] = fmaxf(fmaxf(sred[0][h][1], sred[1][h][1]), fmaxf(sred[2][h][1], sred[3][h][1]));
+    }
+    float lam_raw = p.lam_raw;
+    if (p.lam_seq != nullptr) {
+        const float ls = p.lam_seq[s];
+        lam_raw = ls == INFINITY ? INFINITY : ls / p.scale;
+    }
+    const float cl = p.c_log2;
+    const bool load_all = (p.flags & BSP_FLAG_LOAD_SKIPPED_V) != 0;
+    const bool exp_all = (p.flags & BSP_FLAG_EXP_SKIPPED) != 0;
+    const char *vg = (const char *)p.v + (int64_t)g * p.v_sh * ES;
+    const int64_t vst = p.v_st * ES;
+    const float *Sg = p.S + (int64_t)(g * G) * p.total_k + kbase;
+
+    float acc[GP][EPL];
+    float lsum[GP];
+    int nskip[GP];
+#pragma unroll
+    for (int h = 0; h < GP; ++h) {
+        lsum[h] = 0.f;
+        nskip[h] = 0;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+    }
+    for (int j = j0; j < j1; ++j) {
+        bool keep[GP];
+        bool any = false;
+#pragma unroll
+        for (int h = 0; h < GP; ++h) {
+            keep[h] = false;
+            if (h < G) {
+                const float mj = p.M[((int64_t)(g * G + h) * p.n_seqs + s) * p.J_max + j];
+                keep[h] = !(mpre[h] - mj > lam_raw);  // strict: a gap equal to lambda keeps the block
+                mpre[h] = fmaxf(mpre[h], mj);
+                any = any || keep[h];
+                if (!keep[h]) {
+                    ++nskip[h];
+                    if (tid == 0 && p.bitmap != nullptr)
+                        atomicOr(&p.bitmap[((int64_t)(g * G + h) * p.n_seqs + s) * p.W + (j >> 5)], 1u << (j & 31));
+                }
+            }
+        }
+        if (!any && !load_all) continue;
+        const int kb = j * p.BK;
+        const int rows = min(p.BK, Lk - kb);
+        for (int r0 = w * RPW; r0 < rows; r0 += 4 * RPW) {
+            const int r = r0 + rw;
+            const bool ok = r < rows;
+            const int key = kb + (ok ? r : rows - 1);
+            const u32x4 x = *(const u32x4 *)(dec_row<PAGED>(p, vg, vst, s, kbase, key) + 16 * sub);
+            float vf[EPL];
+            widen16<F8>(x, vf);
+#pragma unroll
+            for (int h = 0; h < GP; ++h) {
+                if (keep[h] && ok) {
+                    const float pe = __builtin_amdgcn_exp2f((Sg[(int64_t)h * p.total_k + key] - mall[h]) * cl);
+                    lsum[h] += pe;
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(pe, vf[e], acc[h][e]);
+                } else if (exp_all && h < G && ok) {
+                    // ablation: the exponential of a skipped key, computed and dropped
+                    const float pe = __builtin_amdgcn_exp2f((Sg[(int64_t)h * p.total_k + key] - mall[h]) * cl);
+                    asm volatile("" ::"v"(pe));
+                }
+            }
+        }
+    }
+    // partial sums: over the rows of this wave (lanes with the same dims), then over the 4 waves
+#pragma unroll
+    for (int h = 0; h < GP; ++h) {
+#pragma unroll
+        for (int m = LPR; m < 64; m <<= 1) {
+            lsum[h] += __shfl_xor(lsum[h], m);
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[h][e] += __shfl_xor(acc[h][e], m);
+        }
+    }
+    if (rw == 0) {
+#pragma unroll
+        for (int h = 0; h < GP; ++h) {
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) sacc[w][h][sub * EPL + e] = acc[h][e];
+            if (sub == 0) sacc[w][h][D] = lsum[h];
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < G * (D + 1) && i < GP * (D + 1); i += 256) {
+        const int h = i / (D + 1), d = i % (D + 1);
+        const float x = (sacc[0][h][d] + sacc[1][h][d]) + (sacc[2][h][d] + sacc[3][h][d]);
+        p.part[(((int64_t)(g * G + h) * p.n_seqs + s) * p.n_chunks + c) * (D + 1) + d] = x;
+    }
+    if (tid == 0) {
+        const unsigned long long vis = (unsigned long long)(j1 - j0);
+        unsigned long long tot = 0;
+#pragma unroll
+        for (int h = 0; h < GP; ++h) {
+            if (h < G) {
+                if (p.skip_count) atomicAdd(&p.skip_count[g * G + h], (unsigned long long)nskip[h]);
+                if (p.visited_count) atomicAdd(&p.visited_count[g * G + h], vis);
+                tot += (unsigned long long)nskip[h];
+            }
+        }
+        if (p.seq_skip) atomicAdd(&p.seq_skip[s], tot);
+        if (p.seq_visited) atomicAdd(&p.seq_visited[s], vis * (unsigned long long)G);
+    }
+}
+
+// o and lse of one (sequence, query head) from the chunk partials.
+template <int D>
+__global__ void __launch_bounds__(64) dec_combine(DecParams p) {
+    const int hq = blockIdx.x % p.Hq, s = blockIdx.x / p.Hq;
+    const int kbase = p.cu_k[s];
+    const int Lk = p.cu_k[s + 1] - kbase;
+    const int nblk = Lk > 0 ? min((Lk + p.BK - 1) / p.BK, p.J_max) : 0;
+    if (nblk == 0) return;  // a sequence without keys: nothing written
+    const int lane = threadIdx.x;
+    const float *Mh = p.M + ((int64_t)hq * p.n_seqs + s) * p.J_max;
+    float mall = -INFINITY;
+    for (int j = lane; j < nblk; j += 64) mall = fmaxf(mall, Mh[j]);
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) mall = fmaxf(mall, __shfl_xor(mall, m));
+    const int nch = (nblk + p.C - 1) / p.C;
+    const float *ph = p.part + ((int64_t)hq * p.n_seqs + s) * p.n_chunks * (D + 1);
+    float l = 0.f;
+    float a[D / 64 > 0 ? D / 64 : 1] = {};
+    for (int c = 0; c < nch; ++c) {
+        l += ph[(int64_t)c * (D + 1) + D];
+#pragma unroll
+        for (int i = 0; i < D / 64; ++i) a[i] += ph[(int64_t)c * (D + 1) + lane + 64 * i];
+    }
+    const float osc = p.v_scale != nullptr ? p.v_scale[hq / p.G] : 1.f;
+    const float inv = osc / l;
+    __bf16 *op = (__bf16 *)p.o + (int64_t)s * p.o_st + (int64_t)hq * p.o_sh;
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) op[lane + 64 * i] = (__bf16)(a[i] * inv);
+    if (lane == 0 && p.lse != nullptr) p.lse[(int64_t)hq * p.lse_sh + s] = (mall * p.c_log2 + __log2f(l)) * kLn2;
+}
+
 // Zero the bitmap and the counters ahead of the main kernel (a plain fill
 // kernel keeps the call free of memset nodes).
 __global__ void __launch_bounds__(256) fill_outputs(uint32_t *bitmap, int64_t words, unsigned long long *c0,
@@ -1214,6 +1578,49 @@ bsp_status_t check_device() {
 }
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ---- decoding step: instances, chunking and workspace layout
+typedef void (*dec_fn)(DecParams);
+struct DecKernels {
+    dec_fn scores, pv, combine;
+};
+template <int IN, int D, bool PAGED, int GP>
+DecKernels dec_kernels() {
+    return {dec_scores<IN, D, PAGED, GP>, dec_pv<IN, D, PAGED, GP>, dec_combine<D>};
+}
+template <int IN, int D, bool PAGED>
+DecKernels dec_by_group(int G) {
+    if (G <= 1) return dec_kernels<IN, D, PAGED, 1>();
+    if (G <= 2) return dec_kernels<IN, D, PAGED, 2>();
+    if (G <= 4) return dec_kernels<IN, D, PAGED, 4>();
+    return dec_kernels<IN, D, PAGED, 8>();
+}
+bool find_dec(int dtype, int D, bool paged, int G, DecKernels &out) {
+    if (G > 8) return false;
+    if (dtype == BSP_BF16 && D == 128) out = paged ? dec_by_group<BSP_BF16, 128, true>(G) : dec_by_group<BSP_BF16, 128, false>(G);
+    else if (dtype == BSP_BF16 && D == 64) out = paged ? dec_by_group<BSP_BF16, 64, true>(G) : dec_by_group<BSP_BF16, 64, false>(G);
+    else if (dtype == BSP_FP8_E4M3 && D == 128) out = paged ? dec_by_group<BSP_FP8_E4M3, 128, true>(G) : dec_by_group<BSP_FP8_E4M3, 128, false>(G);
+    else return false;
+    return true;
+}
+
+// Key blocks per chunk: about 2048 (sequence, KV head, chunk) work items.
+struct DecLayout {
+    int64_t J_max, C, n_chunks, s_off, m_off, part_off, bytes;
+};
+DecLayout dec_layout(int n_heads_q, int n_heads_kv, int n_seqs, int64_t total_k, int max_k, int head_dim, int block_k) {
+    DecLayout L;
+    L.J_max = cdiv(max_k, block_k);
+    const int64_t units = (int64_t)n_seqs * n_heads_kv * L.J_max;
+    L.C = units > 2048 ? cdiv(units, 2048) : 1;
+    L.n_chunks = L.J_max > 0 ? cdiv(L.J_max, L.C) : 0;
+    auto up = [](int64_t x) { return (x + 255) & ~(int64_t)255; };
+    L.s_off = 0;
+    L.m_off = up((int64_t)n_heads_q * total_k * 4);
+    L.part_off = L.m_off + up((int64_t)n_heads_q * n_seqs * L.J_max * 4);
+    L.bytes = L.part_off + up((int64_t)n_heads_q * n_seqs * L.n_chunks * (head_dim + 1) * 4);
+    return L;
+}
 
 }  // namespace
 
@@ -1397,6 +1804,155 @@ bsp_status_t bsp_attn_fwd_ex(const bsp_tensor_t *q, const bsp_tensor_t *k, const
         p.seq_visited = c3;
         p.flags = opts->flags;
         hipLaunchKernelGGL(fn, dim3((unsigned)grid64), dim3(block_q * 2 * hpw), 0, hs, p);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(BSP_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    return BSP_OK;
+}
+
+int64_t bsp_decode_workspace_bytes(int n_heads_q, int n_heads_kv, int n_seqs, int64_t total_k, int max_seqlen_k,
+                                   int head_dim, int block_k) {
+    if (n_heads_q <= 0 || n_heads_kv <= 0 || n_seqs < 0 || total_k < 0 || max_seqlen_k < 0 || head_dim <= 0 ||
+        block_k <= 0)
+        return -1;
+    return dec_layout(n_heads_q, n_heads_kv, n_seqs, total_k, max_seqlen_k, head_dim, block_k).bytes;
+}
+
+bsp_status_t bsp_attn_decode(const bsp_tensor_t *q, const bsp_tensor_t *k, const bsp_tensor_t *v, bsp_tensor_t *o,
+                             float *lse, const bsp_seqs_t *seqs_k, const bsp_block_table_t *bt, int n_heads_q,
+                             int n_heads_kv, int head_dim, int block_k, float lambda, bsp_skip_out_t *skip_out,
+                             void *stream, const bsp_decode_options_t *opts, void *workspace,
+                             int64_t workspace_bytes) {
+    g_detail[0] = '\0';
+    bsp_decode_options_t none;
+    memset(&none, 0, sizeof(none));
+    if (opts == nullptr) opts = &none;
+    if ((opts->flags & ~(BSP_FLAG_LOAD_SKIPPED_V | BSP_FLAG_EXP_SKIPPED)) != 0)
+        return fail(BSP_ERR_INVALID_ARG, "unknown option flags 0x%x", opts->flags);
+    if (opts->lambda_per_seq != nullptr && ((uintptr_t)opts->lambda_per_seq & 3u) != 0)
+        return fail(BSP_ERR_INVALID_ARG, "lambda_per_seq not 4-byte aligned");
+    if (((uintptr_t)opts->skip_count_per_seq & 7u) != 0 || ((uintptr_t)opts->visited_count_per_seq & 7u) != 0)
+        return fail(BSP_ERR_INVALID_ARG, "per-sequence counts not 8-byte aligned");
+    if (n_heads_q <= 0 || n_heads_kv <= 0 || n_heads_q % n_heads_kv != 0)
+        return fail(BSP_ERR_INVALID_ARG, "n_heads_q (%d) must be a positive multiple of n_heads_kv (%d)", n_heads_q,
+                    n_heads_kv);
+    if (head_dim <= 0) return fail(BSP_ERR_INVALID_ARG, "head_dim must be positive");
+    if (isnan(lambda) || lambda < 0.f) return fail(BSP_ERR_INVALID_ARG, "lambda must be >= 0 or +inf (got %g)", lambda);
+    if (block_k <= 0) return fail(BSP_ERR_INVALID_ARG, "block_k must be positive");
+    bsp_status_t st;
+    if ((st = check_tensor("q", q, n_heads_q, head_dim)) != BSP_OK) return st;
+    if ((st = check_tensor("k", k, n_heads_kv, head_dim)) != BSP_OK) return st;
+    if ((st = check_tensor("v", v, n_heads_kv, head_dim)) != BSP_OK) return st;
+    if ((st = check_tensor("o", o, n_heads_q, head_dim)) != BSP_OK) return st;
+    if (k->dtype != q->dtype || v->dtype != q->dtype)
+        return fail(BSP_ERR_INVALID_ARG, "q, k and v must share one dtype");
+    if (q->dtype == BSP_F32) return fail(BSP_ERR_UNSUPPORTED, "decoding supports bf16 and fp8 e4m3 inputs");
+    if (o->dtype != BSP_BF16) return fail(BSP_ERR_INVALID_ARG, "o must be bf16");
+    if (q->dtype == BSP_FP8_E4M3 && (!q->scale || !k->scale || !v->scale))
+        return fail(BSP_ERR_INVALID_ARG, "fp8 inputs need per-head scales on q, k and v");
+    if (seqs_k == nullptr || seqs_k->cu_seqlens == nullptr) return fail(BSP_ERR_INVALID_ARG, "seqs_k->cu_seqlens is required");
+    if (seqs_k->n_seqs < 0 || seqs_k->max_seqlen < 0 || seqs_k->total_tokens < 0)
+        return fail(BSP_ERR_INVALID_ARG, "negative sequence sizes");
+    if (((uintptr_t)seqs_k->cu_seqlens & 3u) != 0) return fail(BSP_ERR_INVALID_ARG, "cu_seqlens not 4-byte aligned");
+    if (lse != nullptr && ((uintptr_t)lse & 3u) != 0) return fail(BSP_ERR_INVALID_ARG, "lse not 4-byte aligned");
+    const bool paged = bt != nullptr;
+    int page_shift = 0;
+    if (paged) {
+        if (bt->table == nullptr) return fail(BSP_ERR_INVALID_ARG, "block_table->table is NULL");
+        const int ps = bt->page_size;
+        if (ps <= 0 || (ps & (ps - 1)) != 0) return fail(BSP_ERR_INVALID_ARG, "page_size must be a power of two");
+        if ((int64_t)bt->max_pages_per_seq * ps < seqs_k->max_seqlen)
+            return fail(BSP_ERR_INVALID_ARG, "max_pages_per_seq * page_size < max_seqlen");
+        while ((1 << page_shift) < ps) ++page_shift;
+    }
+    const int G = n_heads_q / n_heads_kv;
+    DecKernels kern;
+    if (!find_dec(q->dtype, head_dim, paged, G, kern))
+        return fail(BSP_ERR_UNSUPPORTED, "no decode kernel for dtype %d, head_dim %d, %d query heads per KV head",
+                    (int)q->dtype, head_dim, G);
+    const int n_seqs = seqs_k->n_seqs;
+    const DecLayout L = dec_layout(n_heads_q, n_heads_kv, n_seqs, seqs_k->total_tokens, seqs_k->max_seqlen, head_dim,
+                                   block_k);
+    if (workspace == nullptr || workspace_bytes < L.bytes || ((uintptr_t)workspace & 255u) != 0)
+        return fail(BSP_ERR_INVALID_ARG, "workspace needs %lld bytes, 256-byte aligned (got %lld)", (long long)L.bytes,
+                    (long long)workspace_bytes);
+    uint32_t *bitmap = skip_out ? skip_out->bitmap : nullptr;
+    const int64_t words = bsp_skip_bitmap_words_kv(n_heads_q, n_seqs, 1, seqs_k->max_seqlen, 1, block_k);
+    if (bitmap != nullptr) {
+        if (((uintptr_t)bitmap & 3u) != 0) return fail(BSP_ERR_INVALID_ARG, "bitmap not 4-byte aligned");
+        if (skip_out->bitmap_words < words)
+            return fail(BSP_ERR_INVALID_ARG, "bitmap holds %lld words, %lld needed", (long long)skip_out->bitmap_words,
+                        (long long)words);
+    }
+    const int64_t grid = (int64_t)n_seqs * n_heads_kv * L.n_chunks;
+    if (grid > 0x7fffffffLL || (int64_t)n_seqs * n_heads_q > 0x7fffffffLL)
+        return fail(BSP_ERR_INVALID_ARG, "too many work items");
+
+    if ((st = check_device()) != BSP_OK) return st;
+    hipStream_t hs = (hipStream_t)stream;
+    unsigned long long *c0 = skip_out ? skip_out->skip_count : nullptr;
+    unsigned long long *c1 = skip_out ? skip_out->visited_count : nullptr;
+    unsigned long long *c2 = opts->skip_count_per_seq;
+    unsigned long long *c3 = opts->visited_count_per_seq;
+    if (bitmap != nullptr || c0 != nullptr || c1 != nullptr || c2 != nullptr || c3 != nullptr) {
+        int64_t work = words > n_heads_q ? words : n_heads_q;
+        if (work < n_seqs) work = n_seqs;
+        const int blocks = (int)(cdiv(work, 256) < 1024 ? cdiv(work, 256) : 1024);
+        hipLaunchKernelGGL(fill_outputs, dim3(blocks > 0 ? blocks : 1), dim3(256), 0, hs, bitmap, words, c0, c1,
+                           n_heads_q, c2, c3, n_seqs);
+    }
+    if (grid > 0) {
+        DecParams p;
+        memset(&p, 0, sizeof(p));
+        p.q = q->data;
+        p.k = k->data;
+        p.v = v->data;
+        p.o = o->data;
+        p.lse = lse;
+        p.q_st = q->stride_token;
+        p.q_sh = q->stride_head;
+        p.k_st = k->stride_token;
+        p.k_sh = k->stride_head;
+        p.v_st = v->stride_token;
+        p.v_sh = v->stride_head;
+        p.o_st = o->stride_token;
+        p.o_sh = o->stride_head;
+        p.lse_sh = n_seqs;
+        p.total_k = seqs_k->total_tokens;
+        p.cu_k = seqs_k->cu_seqlens;
+        p.table = paged ? bt->table : nullptr;
+        p.max_pages = paged ? bt->max_pages_per_seq : 0;
+        p.page_shift = page_shift;
+        p.bitmap = bitmap;
+        p.skip_count = c0;
+        p.visited_count = c1;
+        p.seq_skip = c2;
+        p.seq_visited = c3;
+        p.n_seqs = n_seqs;
+        p.W = (int32_t)cdiv(L.J_max, 32);
+        p.J_max = (int32_t)L.J_max;
+        p.n_chunks = (int32_t)L.n_chunks;
+        p.C = (int32_t)L.C;
+        p.BK = block_k;
+        p.Hq = n_heads_q;
+        p.Hkv = n_heads_kv;
+        p.G = G;
+        const double scale = 1.0 / sqrt((double)head_dim);
+        p.scale = (float)scale;
+        p.c_log2 = (float)(scale * 1.4426950408889634);
+        p.lam_raw = isinf(lambda) ? INFINITY : (float)((double)lambda / scale);
+        p.lam_seq = opts->lambda_per_seq;
+        p.q_scale = q->scale;
+        p.k_scale = k->scale;
+        p.v_scale = q->dtype == BSP_FP8_E4M3 ? v->scale : nullptr;
+        p.flags = opts->flags;
+        char *ws = (char *)workspace;
+        p.S = (float *)(ws + L.s_off);
+        p.M = (float *)(ws + L.m_off);
+        p.part = (float *)(ws + L.part_off);
+        hipLaunchKernelGGL(kern.scores, dim3((unsigned)grid), dim3(256), 0, hs, p);
+        hipLaunchKernelGGL(kern.pv, dim3((unsigned)grid), dim3(256), 0, hs, p);
+        hipLaunchKernelGGL(kern.combine, dim3((unsigned)((int64_t)n_seqs * n_heads_q)), dim3(64), 0, hs, p);
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(BSP_ERR_HIP, "launch failed: %s", hipGetErrorString(e));

@@ -142,8 +142,9 @@ int64_t bsp_skip_bitmap_words(int n_heads_q, int n_seqs, int max_seqlen, int blo
  * Options of bsp_attn_fwd_ex. Zero-initialise the struct and set what is
  * needed; a NULL options pointer (or an all-zero struct) is bsp_attn_fwd.
  *
- *   - chunked prefill against a cached prefix (the guide's section 3.1: long
- *     prompts are prefilled in chunks): with cu_seqlens_k set, sequence s has
+ *   - chunked prefill against a cached prefix (the FlowPrefill page, "FlowPrefill：
+ *     突破LLM推理瓶颈…", sections 2.1 and 4.5.2: a long prompt is prefilled in
+ *     fixed-size chunks, 8K combining best with its scheduler): with cu_seqlens_k set, sequence s has
  *     Lq = cu_seqlens[s+1]-cu_seqlens[s] query rows (rows of q and o) and
  *     Lk = cu_seqlens_k[s+1]-cu_seqlens_k[s] >= Lq keys/values (rows of k and
  *     v, or positions of its block-table pages). The queries are the last Lq
@@ -192,6 +193,60 @@ bsp_status_t bsp_attn_fwd_ex(const bsp_tensor_t *q, const bsp_tensor_t *k, const
 /* Bitmap words for a call with max_seqlen_k keys per sequence (0 for invalid arguments). */
 int64_t bsp_skip_bitmap_words_kv(int n_heads_q, int n_seqs, int max_seqlen_q, int max_seqlen_k, int block_q,
                                  int block_k);
+
+/*
+ * Decoding step (the guide, section 6.1: a smaller threshold in the decoding
+ * phase; section 7.2: per-token decoding latency is a validation metric): each sequence appends one query row, which sees
+ * all of its Lk keys. The same skip rule applies with the row as its own
+ * tile: key block j is skipped when max over earlier blocks of the block
+ * maximum score minus block j's maximum exceeds lambda (strict); block 0 is
+ * never skipped. The result equals bsp_attn_fwd_ex with one query row per
+ * sequence (cu_seqlens = 0,1,...,n_seqs; cu_seqlens_k = seqs_k->cu_seqlens),
+ * up to rounding.
+ *
+ * Arguments:
+ *   q        [n_seqs, n_heads_q, head_dim]: row s is sequence s's new query
+ *            (stride_token = distance between sequences). bf16, or fp8 e4m3
+ *            with per-head scales as in bsp_attn_fwd.
+ *   k, v     packed [total_tokens, n_heads_kv, head_dim] rows addressed by
+ *            seqs_k->cu_seqlens, or paged through block_table (any
+ *            power-of-two page size; block_k and page_size are independent).
+ *   o        [n_seqs, n_heads_q, head_dim] bf16.  lse: [n_heads_q, n_seqs]
+ *            fp32 natural log, or NULL.
+ *   seqs_k   cu_seqlens (device int32[n_seqs+1]) of the keys including the
+ *            new token, n_seqs, max_seqlen = max Lk, total_tokens =
+ *            cu_seqlens[n_seqs] (rows of the score workspace).
+ *   block_k  decision granularity in keys (any positive value).
+ *   skip_mask_out  bitmap of bsp_skip_bitmap_words_kv(n_heads_q, n_seqs, 1,
+ *            max_seqlen, 1, block_k) words: row h * n_seqs + s, bit j set iff
+ *            block j was skipped; counts per query head as in bsp_attn_fwd.
+ *   options  lambda per sequence, counts per sequence, ablation flags (same
+ *            meaning as in bsp_fwd_options_t), or NULL.
+ *   workspace  caller-owned device memory, 256-byte aligned, of at least
+ *            bsp_decode_workspace_bytes(...) bytes (scores, block maxima and
+ *            partial sums); its contents need no initialisation and are
+ *            overwritten. Concurrent calls need separate workspaces.
+ * Supported: bf16 head_dim 64 or 128, fp8 e4m3 head_dim 128, up to 8 query
+ * heads per KV head (else BSP_ERR_UNSUPPORTED). A sequence with Lk = 0 gets no
+ * output. The call is asynchronous on `stream` (three kernels plus the output
+ * fill) and allocates nothing.
+ */
+typedef struct {
+    const float *lambda_per_seq;                /* device float[n_seqs] or NULL */
+    unsigned long long *skip_count_per_seq;     /* device uint64[n_seqs] or NULL */
+    unsigned long long *visited_count_per_seq;  /* device uint64[n_seqs] or NULL */
+    uint32_t flags;                             /* BSP_FLAG_* */
+} bsp_decode_options_t;
+
+/* Workspace bytes for bsp_attn_decode (-1 for invalid arguments). */
+int64_t bsp_decode_workspace_bytes(int n_heads_q, int n_heads_kv, int n_seqs, int64_t total_k, int max_seqlen_k,
+                                   int head_dim, int block_k);
+
+bsp_status_t bsp_attn_decode(const bsp_tensor_t *q, const bsp_tensor_t *k, const bsp_tensor_t *v,
+                             bsp_tensor_t *o, float *lse, const bsp_seqs_t *seqs_k,
+                             const bsp_block_table_t *block_table, int n_heads_q, int n_heads_kv, int head_dim,
+                             int block_k, float lambda, bsp_skip_out_t *skip_mask_out, void *stream,
+                             const bsp_decode_options_t *options, void *workspace, int64_t workspace_bytes);
 
 /* Static text for a status code. */
 const char *bsp_status_string(int status);

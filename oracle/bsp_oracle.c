@@ -26,8 +26,8 @@
  *     the first block it is -inf, so block 0 is never skipped.
  *   - skipped keys leave both the numerator and the denominator.
  *   - causal masking per sequence: key c is visible to query r iff c <= r.
- *   - chunked prefill against a cached prefix (the guide's section 3.1 on
- *     prefill in chunks): a sequence's queries are the LAST Lq of its Lk
+ *   - chunked prefill against a cached prefix (the FlowPrefill page, sections
+ *     2.1 and 4.5.2, on prefill in fixed-size chunks): a sequence's queries are the LAST Lq of its Lk
  *     keys (bottom-right alignment), so query row r of the chunk sits at key
  *     position (Lk - Lq) + r and sees keys 0 .. (Lk - Lq) + r. Lq = Lk is the
  *     plain prefill.

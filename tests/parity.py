@@ -80,7 +80,8 @@ class Chunk:
 
 
 def run_gpu(inp: synth.Inputs, dev: Dict, block_q: int, block_k: int, lam: float, paged: bool = False,
-            chunk: Optional[Chunk] = None, lam_seq: Optional[Sequence[float]] = None, flags: int = 0):
+            chunk: Optional[Chunk] = None, lam_seq: Optional[Sequence[float]] = None, flags: int = 0,
+            decode: bool = False):
     import torch
 
     import block_sparse_long_bsp_amd as bsp
@@ -88,6 +89,24 @@ def run_gpu(inp: synth.Inputs, dev: Dict, block_q: int, block_k: int, lam: float
     k = dev["k_pages"] if paged else dev["k"]
     v = dev["v_pages"] if paged else dev["v"]
     n_seqs = len(inp.seqlens)
+    if decode:
+        # bsp_attn_decode: the last row of every sequence against all of its keys
+        # (the chunk-of-one case of the oracle)
+        assert chunk is not None and all(n == 1 for n in chunk.lq)
+        q = dev["q"][torch.from_numpy(chunk.rows(inp)).to(dev["q"].device)].contiguous()
+        seq_sc = torch.empty(n_seqs, dtype=torch.int64, device=q.device)
+        seq_vc = torch.empty(n_seqs, dtype=torch.int64, device=q.device)
+        lps = None if lam_seq is None else torch.tensor(list(lam_seq), dtype=torch.float32, device=q.device)
+        o, lse, bitmap, sc, vc = bsp.decode(q, k, v, dev["cu"], inp.max_seqlen, total_k=inp.total_tokens,
+                                            block_table=dev.get("table") if paged else None, block_k=block_k,
+                                            lam=lam, q_scale=dev["q_scale"], k_scale=dev["k_scale"],
+                                            v_scale=dev["v_scale"], lam_per_seq=lps, seq_skip_count=seq_sc,
+                                            seq_visited_count=seq_vc, flags=flags)
+        torch.cuda.synchronize()
+        return dict(o=o.float().cpu().numpy(), lse=lse.cpu().numpy(),
+                    bits=bsp.unpack_bitmap(bitmap, inp.q.shape[1], n_seqs, 1, 1, block_k, inp.max_seqlen),
+                    skip_count=sc.cpu().numpy(), visited_count=vc.cpu().numpy(),
+                    seq_skip_count=seq_sc.cpu().numpy(), seq_visited_count=seq_vc.cpu().numpy())
     kw = {}
     q, cu, max_q = dev["q"], dev["cu"], inp.max_seqlen
     if chunk is not None:
@@ -227,12 +246,13 @@ def compare(inp: synth.Inputs, gpu: Dict, block_q: int, block_k: int, lam: float
 
 def check_case(inp: synth.Inputs, block_q: int, block_k: int, lams: Sequence[float], paged: bool = False,
                work: Optional[np.ndarray] = None, dev=None, chunk: Optional[Chunk] = None,
-               lam_seq: Optional[Sequence[float]] = None, flags: int = 0) -> List[Report]:
+               lam_seq: Optional[Sequence[float]] = None, flags: int = 0, decode: bool = False) -> List[Report]:
     """Run the GPU for each lambda and compare; raise AssertionError on any problem."""
     dev = dev or to_device(inp)
     reps = []
     for lam in lams:
-        gpu = run_gpu(inp, dev, block_q, block_k, lam, paged=paged, chunk=chunk, lam_seq=lam_seq, flags=flags)
+        gpu = run_gpu(inp, dev, block_q, block_k, lam, paged=paged, chunk=chunk, lam_seq=lam_seq, flags=flags,
+                      decode=decode)
         rep = compare(inp, gpu, block_q, block_k, lam, work=work, chunk=chunk, lam_seq=lam_seq)
         reps.append(rep)
         assert rep.ok(), f"lambda={lam}: " + "; ".join(rep.problems)

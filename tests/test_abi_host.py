@@ -73,6 +73,9 @@ int main(void) {
   printf("%zu %zu %zu %zu %zu %zu\n", sizeof(bsp_fwd_options_t), offsetof(bsp_fwd_options_t, max_seqlen_k),
          offsetof(bsp_fwd_options_t, lambda_per_seq), offsetof(bsp_fwd_options_t, skip_count_per_seq),
          offsetof(bsp_fwd_options_t, visited_count_per_seq), offsetof(bsp_fwd_options_t, flags));
+  printf("%zu %zu %zu %zu %zu %zu\n", sizeof(bsp_decode_options_t), offsetof(bsp_decode_options_t, lambda_per_seq),
+         offsetof(bsp_decode_options_t, skip_count_per_seq), offsetof(bsp_decode_options_t, visited_count_per_seq),
+         offsetof(bsp_decode_options_t, flags), (size_t)0);
   return 0;
 }
 '''
@@ -91,6 +94,9 @@ int main(void) {
     O = bsp.Options
     assert vals[3] == [ctypes.sizeof(O), O.max_seqlen_k.offset, O.lambda_per_seq.offset, O.skip_count_per_seq.offset,
                        O.visited_count_per_seq.offset, O.flags.offset]
+    DO = bsp.DecodeOptions
+    assert vals[4][:5] == [ctypes.sizeof(DO), DO.lambda_per_seq.offset, DO.skip_count_per_seq.offset,
+                           DO.visited_count_per_seq.offset, DO.flags.offset]
 
 
 def test_bitmap_words_formula(lib):
@@ -213,3 +219,73 @@ def test_binding_fails_loudly_without_library(tmp_path):
     r = subprocess.run(["python", "-c", "import block_sparse_long_bsp_amd as b; b.load_library('/nonexistent/lib.so')"],
                        capture_output=True, text=True, cwd=ROOT)
     assert r.returncode != 0 and "missing" in r.stderr
+
+
+# ------------------------------------------------------------------ decoding step
+
+def test_decode_workspace_bytes(lib):
+    # scores [Hq][total_k] + block maxima [Hq][n_seqs][J] + partials [Hq][n_seqs][chunks][D+1], 256-byte aligned parts
+    n = bsp.decode_workspace_bytes(32, 8, 1, 32768, 32768, 128, 128)
+    J = 256
+    chunks = 256  # 1 x 8 x 256 units need no grouping of blocks
+    assert n == 32 * 32768 * 4 + 32 * J * 4 + 32 * chunks * 129 * 4
+    # many sequences: blocks are grouped so that about 2048 work items remain
+    n16 = bsp.decode_workspace_bytes(32, 8, 16, 16 * 20000, 32768, 128, 128)
+    assert n16 >= 32 * 16 * 20000 * 4 + 32 * 16 * 256 * 4
+    assert bsp.decode_workspace_bytes(32, 8, 1, 100, 100, 128, 0) == -1
+    assert bsp.decode_workspace_bytes(0, 8, 1, 100, 100, 128, 128) == -1
+
+
+def _call_dec(**over):
+    D, Hq, Hkv = over.pop("D", 128), over.pop("Hq", 32), over.pop("Hkv", 8)
+    dt = over.pop("dtype", bsp.BSP_BF16)
+    scale = over.pop("scale", None)
+    q = Tensor(FAKE, dt, Hq * D, D, scale)
+    kv = Tensor(FAKE, dt, Hkv * D, D, scale)
+    o = over.pop("o", Tensor(FAKE, bsp.BSP_BF16, Hq * D, D, None))
+    seqs = over.pop("seqs", Seqs(FAKE, 2, 4096, 5000))
+    bt = over.pop("bt", None)
+    bk = over.pop("block_k", 128)
+    lam = over.pop("lam", 3.0)
+    need = bsp.decode_workspace_bytes(Hq, Hkv, seqs.n_seqs, seqs.total_tokens, seqs.max_seqlen, D, bk)
+    ws = over.pop("ws", FAKE)
+    ws_bytes = over.pop("ws_bytes", need)
+    so = over.pop("so", SkipOut(FAKE, bsp.skip_bitmap_words_kv(Hq, seqs.n_seqs, 1, seqs.max_seqlen, 1, bk), FAKE, FAKE))
+    opts = over.pop("opts", None)
+    assert not over
+    return int(lib_handle().bsp_attn_decode(ctypes.byref(q), ctypes.byref(kv), ctypes.byref(kv), ctypes.byref(o),
+                                            ctypes.c_void_p(FAKE), ctypes.byref(seqs),
+                                            ctypes.byref(bt) if bt is not None else None, Hq, Hkv, D, bk,
+                                            ctypes.c_float(lam), ctypes.byref(so), None,
+                                            ctypes.byref(opts) if opts is not None else None,
+                                            ctypes.c_void_p(ws), ctypes.c_int64(ws_bytes)))
+
+
+def lib_handle():
+    return bsp.load_library()
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(ws=0), bsp.BSP_ERR_INVALID_ARG),                               # no workspace
+    (dict(ws_bytes=1024), bsp.BSP_ERR_INVALID_ARG),                      # too small
+    (dict(ws=FAKE + 16), bsp.BSP_ERR_INVALID_ARG),                       # not 256-byte aligned
+    (dict(lam=-1.0), bsp.BSP_ERR_INVALID_ARG),
+    (dict(block_k=0), bsp.BSP_ERR_INVALID_ARG),
+    (dict(Hq=30), bsp.BSP_ERR_INVALID_ARG),
+    (dict(seqs=Seqs(0, 2, 4096, 5000)), bsp.BSP_ERR_INVALID_ARG),
+    (dict(so=SkipOut(FAKE, 3, None, None)), bsp.BSP_ERR_INVALID_ARG),    # bitmap too small
+    (dict(bt=BlockTable(FAKE, 2, 64)), bsp.BSP_ERR_INVALID_ARG),         # pages cannot hold max_seqlen
+    (dict(bt=BlockTable(FAKE, 64, 48)), bsp.BSP_ERR_INVALID_ARG),        # page size not a power of two
+    (dict(o=Tensor(FAKE, bsp.BSP_F32, 32 * 128, 128, None)), bsp.BSP_ERR_INVALID_ARG),
+    (dict(dtype=bsp.BSP_F32, o=Tensor(FAKE, bsp.BSP_F32, 32 * 128, 128, None)), bsp.BSP_ERR_UNSUPPORTED),
+    (dict(dtype=bsp.BSP_FP8_E4M3), bsp.BSP_ERR_INVALID_ARG),             # fp8 without scales
+    (dict(dtype=bsp.BSP_FP8_E4M3, scale=FAKE, D=64, o=Tensor(FAKE, bsp.BSP_BF16, 32 * 64, 64, None)),
+     bsp.BSP_ERR_UNSUPPORTED),
+    (dict(Hq=80, Hkv=8, o=Tensor(FAKE, bsp.BSP_BF16, 80 * 128, 128, None)), bsp.BSP_ERR_UNSUPPORTED),  # 10 heads per KV head
+    (dict(opts=bsp.DecodeOptions(None, None, None, 8)), bsp.BSP_ERR_INVALID_ARG),   # unknown flag
+    (dict(opts=bsp.DecodeOptions(FAKE + 2, None, None, 0)), bsp.BSP_ERR_INVALID_ARG),
+])
+def test_decode_invalid_arguments_rejected_before_the_device(lib, case, expect):
+    st = _call_dec(**case)
+    assert st == expect, (st, bsp.last_error_detail())
+    assert bsp.last_error_detail() != ""

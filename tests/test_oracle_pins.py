@@ -437,7 +437,7 @@ def test_invalid_arguments_rejected():
 
 # ------------------------------------------ chunked prefill, per-sequence lambda --
 # The queries of a sequence may be the last Lq of its Lk positions (prefill in
-# chunks against a cached prefix, the guide's section 3.1): query row r of the
+# chunks against a cached prefix, the FlowPrefill page, sections 2.1 and 4.5.2): query row r of the
 # chunk sits at key position (Lk - Lq) + r. Pinned against numpy and brute force
 # written with that offset, and against the plain prefill of the whole sequence.
 
