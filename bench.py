@@ -355,6 +355,51 @@ def main():
                              "kv_gbs": kv_bytes / (ms_c * 1e-3) / 1e9 if lq == 1 else None})
         result["chunked"] = rows
 
+        # ---- decoding steps (bsp_attn_decode): one new query row per sequence.
+        # Algorithmic HBM bytes: K of every key, V of the blocks some query head of
+        # the KV group keeps (here: of every block for lambda = +inf).
+        dec = []
+        es = k.element_size()
+        kv_row_bytes = w.n_heads_kv * D * es
+        cu1 = torch.tensor([0, L], dtype=torch.int32, device="cuda")
+        q1 = q[L - 1:].contiguous()
+        ws1 = torch.empty(bsp.decode_workspace_bytes(H, w.n_heads_kv, 1, L, L, D, w.block_k), dtype=torch.uint8,
+                          device="cuda")
+        sc1 = torch.empty(H, dtype=torch.int64, device="cuda")
+        vc1 = torch.empty(H, dtype=torch.int64, device="cuda")
+        for lam in [dense_lam] + [x for x in (5.3,) if finite] + finite[-1:]:
+            def fn(lam=lam):
+                return bsp.decode(q1, k, v, cu1, L, block_k=w.block_k, lam=lam, q_scale=scales[0],
+                                  k_scale=scales[1], v_scale=scales[2], want_bitmap=False, skip_count=sc1,
+                                  visited_count=vc1, workspace=ws1)
+            ms_d = time_calls(fn, args.extra_steps * 5, 5)
+            f = int(sc1.sum().item()) / max(1, int(vc1.sum().item()))
+            byts = L * kv_row_bytes * (2.0 - f)  # V skipped only where every head of a group skips: an upper bound
+            dec.append({"batch": 1, "lk": L, "lambda": lam, "ms": ms_d, "tokens_per_s": 1.0 / (ms_d * 1e-3),
+                        "skip_fraction": f, "kv_gbs_upper": byts / (ms_d * 1e-3) / 1e9})
+        # a batch of 16 contexts of the same length, distinct pages of random data (lambda = +inf)
+        B, page = 16, 64
+        n_pages = B * L // page
+        kp = torch.randn((n_pages, page, w.n_heads_kv, D), device="cuda").to(k.dtype)
+        vp = torch.randn((n_pages, page, w.n_heads_kv, D), device="cuda").to(k.dtype)
+        table = torch.randperm(n_pages, device="cuda", dtype=torch.int64).to(torch.int32).view(B, L // page).contiguous()
+        cuB = torch.arange(0, (B + 1) * L, L, dtype=torch.int32, device="cuda")
+        qB = torch.randn((B, H, D), device="cuda").to(q.dtype)
+        wsB = torch.empty(bsp.decode_workspace_bytes(H, w.n_heads_kv, B, B * L, L, D, w.block_k), dtype=torch.uint8,
+                          device="cuda")
+
+        def fnB():
+            return bsp.decode(qB, kp, vp, cuB, L, total_k=B * L, block_table=table, block_k=w.block_k, lam=dense_lam,
+                              q_scale=scales[0], k_scale=scales[1], v_scale=scales[2], want_bitmap=False,
+                              workspace=wsB)
+        ms_b = time_calls(fnB, args.extra_steps * 2, 3)
+        byts = B * L * kv_row_bytes * 2.0
+        dec.append({"batch": B, "lk": L, "lambda": dense_lam, "paged": page, "ms": ms_b, "tokens_per_s": B / (ms_b * 1e-3),
+                    "skip_fraction": 0.0, "kv_gbs": byts / (ms_b * 1e-3) / 1e9,
+                    "hbm_frac": byts / (ms_b * 1e-3) / 1e9 / HBM_GBS, "data": "random normal (timing only)"})
+        del kp, vp, wsB
+        result["decode"] = dec
+
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, w, dense_lam, target_s=args.cpu_seconds)
     else:

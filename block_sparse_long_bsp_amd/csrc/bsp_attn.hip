@@ -1116,6 +1116,9 @@ __global__ void __launch_bounds__(BQ * 2) fwd_f32(FwdParams p) {
 // the KV group keeps, the scores written and read once. All vector ALU: four
 // query heads per KV head are too few rows for the matrix cores.
 // ---------------------------------------------------------------------------
+constexpr int kDecRows = 8;    // K/V row loads per wave in flight in the decode kernels
+constexpr int kDecMaxC = 256;  // key blocks per decode chunk, at most
+
 struct DecParams {
     const void *q, *k, *v;
     void *o;
@@ -1133,7 +1136,7 @@ struct DecParams {
     const float *lam_seq;
     const float *q_scale, *k_scale, *v_scale;
     uint32_t flags;
-    float *S;     // [Hq][total_k]
+    float *S;     // [Hkv][total_k][GP]: scores of the GP (padded) query heads of a KV head, key-major
     float *M;     // [Hq][n_seqs][J_max]
     float *part;  // [Hq][n_seqs][n_chunks][D + 1]: sum p*v over the chunk, then sum p
 };
@@ -1156,6 +1159,47 @@ __device__ __forceinline__ float row_sum(float x) {
     x += dpp(x, 2);
     if constexpr (LPR == 16) x += dpp(x, 3);
     return x;
+}
+
+// Row sums of NH values at once (one DPP step for every value before the next
+// step, so no step waits on the one just issued).
+template <int LPR, int NH>
+__device__ __forceinline__ void row_sums(float *x) {
+    auto step = [&](int ctrl) {
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+            const float xh = x[h];
+            const int v = __builtin_bit_cast(int, xh);
+            int y;
+            if (ctrl == 0) y = __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true);        // lane ^ 1
+            else if (ctrl == 1) y = __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true);   // lane ^ 2
+            else if (ctrl == 2) y = __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, true);  // mirror in 8
+            else y = __builtin_amdgcn_mov_dpp(v, 0x140, 0xF, 0xF, true);                 // mirror in 16
+            x[h] += __builtin_bit_cast(float, y);
+        }
+    };
+    step(0);
+    step(1);
+    step(2);
+    if constexpr (LPR == 16) step(3);
+}
+
+// 16 bytes of a row as packed bf16 pairs: 4 words for bf16, 8 for e4m3 codes
+// (each pair widened exactly).
+template <bool F8>
+__device__ __forceinline__ void pairs16(const u32x4 x, bf16x2 *w) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if constexpr (F8) {
+            w[2 * i] = __builtin_bit_cast(bf16x2, fp8x2_to_bf16x2<false>(x[i]));
+            w[2 * i + 1] = __builtin_bit_cast(bf16x2, fp8x2_to_bf16x2<true>(x[i]));
+        } else {
+            // (through a scalar: a bit_cast applied directly to a vector element
+            // reads element 0 for every i with this compiler)
+            const uint32_t xi = x[i];
+            w[i] = __builtin_bit_cast(bf16x2, xi);
+        }
+    }
 }
 
 // 16 bytes of a row as fp32: 8 bf16 values, or 16 e4m3 codes (widened exactly).
@@ -1188,14 +1232,16 @@ __device__ __forceinline__ const char *dec_row(const DecParams &p, const char *b
     }
 }
 
-// Work item of the decode kernels: (sequence, KV head, chunk of C key blocks).
+// Work item of the decode kernels: (sequence, chunk of C key blocks, KV head),
+// KV head fastest: neighbouring workgroups read the same key rows (which hold
+// all KV heads side by side), so DRAM pages are read once, not once per head.
 __device__ __forceinline__ bool dec_item(const DecParams &p, int &s, int &g, int &c, int &kbase, int &Lk, int &nblk,
                                          int &j0, int &j1) {
     int item = blockIdx.x;
-    c = item % p.n_chunks;
-    item /= p.n_chunks;
     g = item % p.Hkv;
-    s = item / p.Hkv;
+    item /= p.Hkv;
+    c = item % p.n_chunks;
+    s = item / p.n_chunks;
     kbase = p.cu_k[s];
     Lk = p.cu_k[s + 1] - kbase;
     nblk = Lk > 0 ? min((Lk + p.BK - 1) / p.BK, p.J_max) : 0;
@@ -1219,61 +1265,69 @@ __global__ void __launch_bounds__(256) dec_scores(DecParams p) {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int sub = lane % LPR, rw = lane / LPR;
     const int G = p.G;
-    float qv[GP][EPL];
+    constexpr int NPR = EPL / 2;  // bf16 pairs per lane per row
+    bf16x2 qp[GP][NPR];
     float sqk[GP];
 #pragma unroll
     for (int h = 0; h < GP; ++h) {
         const int hq = g * G + (h < G ? h : 0);
         const u32x4 x = *(const u32x4 *)((const char *)p.q + ((int64_t)s * p.q_st + (int64_t)hq * p.q_sh) * ES + 16 * sub);
-        widen16<F8>(x, qv[h]);
+        pairs16<F8>(x, qp[h]);
         sqk[h] = F8 ? p.q_scale[hq] * p.k_scale[g] : 1.f;
     }
     const char *kg = (const char *)p.k + (int64_t)g * p.k_sh * ES;
     const int64_t kst = p.k_st * ES;
-    __shared__ float smax[4][GP];
-    for (int j = j0; j < j1; ++j) {
+    float *Sg = p.S + ((int64_t)g * p.total_k + kbase) * GP;
+    // the chunk's blocks go round-robin to the 4 waves; a wave reduces its block alone
+    for (int j = j0 + w; j < j1; j += 4) {
         const int kb = j * p.BK;
         const int rows = min(p.BK, Lk - kb);
         float bmax[GP];
 #pragma unroll
         for (int h = 0; h < GP; ++h) bmax[h] = -INFINITY;
-        for (int r0 = w * RPW; r0 < rows; r0 += 4 * RPW) {
-            const int r = r0 + rw;
-            const bool ok = r < rows;
-            const int key = kb + (ok ? r : rows - 1);
-            const u32x4 x = *(const u32x4 *)(dec_row<PAGED>(p, kg, kst, s, kbase, key) + 16 * sub);
-            float kf[EPL];
-            widen16<F8>(x, kf);
+        // kDecRows row loads in flight (rows past the block re-read its last row)
+        for (int r0 = 0; r0 < rows; r0 += RPW * kDecRows) {
+            u32x4 xs[kDecRows];
 #pragma unroll
-            for (int h = 0; h < GP; ++h) {
-                float d = 0.f;
+            for (int u = 0; u < kDecRows; ++u) {
+                const int r = r0 + RPW * u + rw;
+                xs[u] = *(const u32x4 *)(dec_row<PAGED>(p, kg, kst, s, kbase, kb + min(r, rows - 1)) + 16 * sub);
+            }
 #pragma unroll
-                for (int e = 0; e < EPL; ++e) d = fmaf(qv[h][e], kf[e], d);
-                d = row_sum<LPR>(d) * sqk[h];
-                if (ok) {
-                    bmax[h] = fmaxf(bmax[h], d);
-                    if (sub == h && h < G) p.S[(int64_t)(g * G + h) * p.total_k + kbase + kb + r] = d;
+            for (int u = 0; u < kDecRows; ++u) {
+                const int r = r0 + RPW * u + rw;
+                const bool ok = r < rows;
+                bf16x2 kp[NPR];
+                pairs16<F8>(xs[u], kp);
+                float d[GP];
+#pragma unroll
+                for (int h = 0; h < GP; ++h) {
+                    d[h] = 0.f;
+#pragma unroll
+                    for (int i = 0; i < NPR; ++i) d[h] = __builtin_amdgcn_fdot2_f32_bf16(kp[i], qp[h][i], d[h], false);
                 }
+                row_sums<LPR, GP>(d);
+                float mine = 0.f;  // lane sub < GP stores head sub's score of the row
+#pragma unroll
+                for (int h = 0; h < GP; ++h) {
+                    d[h] *= sqk[h];
+                    bmax[h] = fmaxf(bmax[h], ok ? d[h] : -INFINITY);
+                    mine = sub == h ? d[h] : mine;
+                }
+                if (ok && sub < GP) Sg[(int64_t)(kb + r) * GP + sub] = mine;
             }
         }
-        // block maxima: over the rows of this wave, then over the 4 waves
 #pragma unroll
         for (int h = 0; h < GP; ++h) {
 #pragma unroll
             for (int m = LPR; m < 64; m <<= 1) bmax[h] = fmaxf(bmax[h], __shfl_xor(bmax[h], m));
         }
-        if (lane == 0) {
+        if (lane < G) {
+            float m = bmax[0];
 #pragma unroll
-            for (int h = 0; h < GP; ++h) smax[w][h] = bmax[h];
+            for (int h = 1; h < GP; ++h) m = lane == h ? bmax[h] : m;
+            p.M[((int64_t)(g * G + lane) * p.n_seqs + s) * p.J_max + j] = m;
         }
-        __syncthreads();
-        if (tid < G && tid < GP) {
-            float m = smax[0][tid];
-#pragma unroll
-            for (int x = 1; x < 4; ++x) m = fmaxf(m, smax[x][tid]);
-            p.M[((int64_t)(g * G + tid) * p.n_seqs + s) * p.J_max + j] = m;
-        }
-        __syncthreads();
     }
 }
 
@@ -1337,57 +1391,93 @@ __global__ void __launch_bounds__(256) dec_pv(DecParams p) {
     const bool exp_all = (p.flags & BSP_FLAG_EXP_SKIPPED) != 0;
     const char *vg = (const char *)p.v + (int64_t)g * p.v_sh * ES;
     const int64_t vst = p.v_st * ES;
-    const float *Sg = p.S + (int64_t)(g * G) * p.total_k + kbase;
+    const float *Sg = p.S + ((int64_t)g * p.total_k + kbase) * GP;
+
+    // the chunk's decisions, block by block in order, one thread per head
+    __shared__ uint8_t skeep[GP][kDecMaxC];
+    unsigned long long nskip = 0;
+    if (tid < G && tid < GP) {
+        const int h = tid;
+        float m = -INFINITY;
+#pragma unroll
+        for (int x = 0; x < GP; ++x) m = x == h ? mpre[x] : m;
+        const float *Mh = p.M + ((int64_t)(g * G + h) * p.n_seqs + s) * p.J_max;
+        for (int j = j0; j < j1; ++j) {
+            const float mj = Mh[j];
+            const bool keep = !(m - mj > lam_raw);  // strict: a gap equal to lambda keeps the block
+            m = fmaxf(m, mj);
+            skeep[h][j - j0] = keep ? 1 : 0;
+            if (!keep) {
+                ++nskip;
+                if (p.bitmap != nullptr)
+                    atomicOr(&p.bitmap[((int64_t)(g * G + h) * p.n_seqs + s) * p.W + (j >> 5)], 1u << (j & 31));
+            }
+        }
+    }
+    __syncthreads();
 
     float acc[GP][EPL];
     float lsum[GP];
-    int nskip[GP];
 #pragma unroll
     for (int h = 0; h < GP; ++h) {
         lsum[h] = 0.f;
-        nskip[h] = 0;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
     }
-    for (int j = j0; j < j1; ++j) {
-        bool keep[GP];
+    // the chunk's blocks go round-robin to the 4 waves
+    for (int j = j0 + w; j < j1; j += 4) {
+        bool keep[GP];  // wave-uniform (read through readfirstlane so that the branches below are scalar)
         bool any = false;
 #pragma unroll
         for (int h = 0; h < GP; ++h) {
-            keep[h] = false;
-            if (h < G) {
-                const float mj = p.M[((int64_t)(g * G + h) * p.n_seqs + s) * p.J_max + j];
-                keep[h] = !(mpre[h] - mj > lam_raw);  // strict: a gap equal to lambda keeps the block
-                mpre[h] = fmaxf(mpre[h], mj);
-                any = any || keep[h];
-                if (!keep[h]) {
-                    ++nskip[h];
-                    if (tid == 0 && p.bitmap != nullptr)
-                        atomicOr(&p.bitmap[((int64_t)(g * G + h) * p.n_seqs + s) * p.W + (j >> 5)], 1u << (j & 31));
-                }
-            }
+            keep[h] = h < G && __builtin_amdgcn_readfirstlane((int)skeep[h][j - j0]) != 0;
+            any = any || keep[h];
         }
         if (!any && !load_all) continue;
         const int kb = j * p.BK;
         const int rows = min(p.BK, Lk - kb);
-        for (int r0 = w * RPW; r0 < rows; r0 += 4 * RPW) {
-            const int r = r0 + rw;
-            const bool ok = r < rows;
-            const int key = kb + (ok ? r : rows - 1);
-            const u32x4 x = *(const u32x4 *)(dec_row<PAGED>(p, vg, vst, s, kbase, key) + 16 * sub);
-            float vf[EPL];
-            widen16<F8>(x, vf);
+        for (int r0 = 0; r0 < rows; r0 += RPW * kDecRows) {
+            u32x4 xs[kDecRows];
+            float sc[kDecRows][GP];
 #pragma unroll
-            for (int h = 0; h < GP; ++h) {
-                if (keep[h] && ok) {
-                    const float pe = __builtin_amdgcn_exp2f((Sg[(int64_t)h * p.total_k + key] - mall[h]) * cl);
-                    lsum[h] += pe;
+            for (int u = 0; u < kDecRows; ++u) {
+                const int key = kb + min(r0 + RPW * u + rw, rows - 1);
+                xs[u] = *(const u32x4 *)(dec_row<PAGED>(p, vg, vst, s, kbase, key) + 16 * sub);
+                // the GP scores of the row in one load
+                if constexpr (GP == 1) {
+                    sc[u][0] = Sg[key];
+                } else if constexpr (GP == 2) {
+                    const u32x2 y = *(const u32x2 *)(Sg + (int64_t)key * 2);
+                    const uint32_t y0 = y[0], y1 = y[1];
+                    sc[u][0] = __builtin_bit_cast(float, y0);
+                    sc[u][1] = __builtin_bit_cast(float, y1);
+                } else {
 #pragma unroll
-                    for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(pe, vf[e], acc[h][e]);
-                } else if (exp_all && h < G && ok) {
-                    // ablation: the exponential of a skipped key, computed and dropped
-                    const float pe = __builtin_amdgcn_exp2f((Sg[(int64_t)h * p.total_k + key] - mall[h]) * cl);
-                    asm volatile("" ::"v"(pe));
+                    for (int h4 = 0; h4 < GP; h4 += 4) {
+                        const f32x4 y = *(const f32x4 *)(Sg + (int64_t)key * GP + h4);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) sc[u][h4 + i] = y[i];
+                    }
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kDecRows; ++u) {
+                const bool ok = r0 + RPW * u + rw < rows;
+                float vf[EPL];
+                widen16<F8>(xs[u], vf);
+#pragma unroll
+                for (int h = 0; h < GP; ++h) {
+                    if (keep[h]) {
+                        const float e2 = __builtin_amdgcn_exp2f((sc[u][h] - mall[h]) * cl);
+                        const float pe = ok ? e2 : 0.f;  // rows past the block end add nothing
+                        lsum[h] += pe;
+#pragma unroll
+                        for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(pe, vf[e], acc[h][e]);
+                    } else if (exp_all && h < G) {
+                        // ablation: the exponential of a skipped key, computed and dropped
+                        const float pe = __builtin_amdgcn_exp2f((sc[u][h] - mall[h]) * cl);
+                        asm volatile("" ::"v"(pe));
+                    }
                 }
             }
         }
@@ -1416,50 +1506,76 @@ __global__ void __launch_bounds__(256) dec_pv(DecParams p) {
         const float x = (sacc[0][h][d] + sacc[1][h][d]) + (sacc[2][h][d] + sacc[3][h][d]);
         p.part[(((int64_t)(g * G + h) * p.n_seqs + s) * p.n_chunks + c) * (D + 1) + d] = x;
     }
-    if (tid == 0) {
+    if (tid < G && tid < GP) {
         const unsigned long long vis = (unsigned long long)(j1 - j0);
-        unsigned long long tot = 0;
-#pragma unroll
-        for (int h = 0; h < GP; ++h) {
-            if (h < G) {
-                if (p.skip_count) atomicAdd(&p.skip_count[g * G + h], (unsigned long long)nskip[h]);
-                if (p.visited_count) atomicAdd(&p.visited_count[g * G + h], vis);
-                tot += (unsigned long long)nskip[h];
-            }
-        }
-        if (p.seq_skip) atomicAdd(&p.seq_skip[s], tot);
-        if (p.seq_visited) atomicAdd(&p.seq_visited[s], vis * (unsigned long long)G);
+        if (p.skip_count) atomicAdd(&p.skip_count[g * G + tid], nskip);
+        if (p.visited_count) atomicAdd(&p.visited_count[g * G + tid], vis);
+        if (p.seq_skip) atomicAdd(&p.seq_skip[s], nskip);
+        if (p.seq_visited) atomicAdd(&p.seq_visited[s], vis);
     }
 }
 
-// o and lse of one (sequence, query head) from the chunk partials.
+// o and lse of one (sequence, query head) from the chunk partials: four waves
+// take every fourth chunk, lanes take dimensions, then the waves add up.
 template <int D>
-__global__ void __launch_bounds__(64) dec_combine(DecParams p) {
+__global__ void __launch_bounds__(256) dec_combine(DecParams p) {
+    constexpr int DL = D / 64;  // dimensions per lane
     const int hq = blockIdx.x % p.Hq, s = blockIdx.x / p.Hq;
     const int kbase = p.cu_k[s];
     const int Lk = p.cu_k[s + 1] - kbase;
     const int nblk = Lk > 0 ? min((Lk + p.BK - 1) / p.BK, p.J_max) : 0;
     if (nblk == 0) return;  // a sequence without keys: nothing written
-    const int lane = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    __shared__ float sm[4];
+    __shared__ float sa[4][D + 1];
     const float *Mh = p.M + ((int64_t)hq * p.n_seqs + s) * p.J_max;
     float mall = -INFINITY;
-    for (int j = lane; j < nblk; j += 64) mall = fmaxf(mall, Mh[j]);
+    for (int j = tid; j < nblk; j += 256) mall = fmaxf(mall, Mh[j]);
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) mall = fmaxf(mall, __shfl_xor(mall, m));
+    if (lane == 0) sm[w] = mall;
     const int nch = (nblk + p.C - 1) / p.C;
     const float *ph = p.part + ((int64_t)hq * p.n_seqs + s) * p.n_chunks * (D + 1);
     float l = 0.f;
-    float a[D / 64 > 0 ? D / 64 : 1] = {};
-    for (int c = 0; c < nch; ++c) {
-        l += ph[(int64_t)c * (D + 1) + D];
+    float a[DL] = {};
+    int c = w;
+    for (; c + 12 < nch; c += 16) {  // four chunks of this wave in flight
+        float lv[4], av[4][DL];
 #pragma unroll
-        for (int i = 0; i < D / 64; ++i) a[i] += ph[(int64_t)c * (D + 1) + lane + 64 * i];
+        for (int u = 0; u < 4; ++u) {
+            const float *pc = ph + (int64_t)(c + 4 * u) * (D + 1);
+            lv[u] = pc[D];
+#pragma unroll
+            for (int i = 0; i < DL; ++i) av[u][i] = pc[lane + 64 * i];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            l += lv[u];
+#pragma unroll
+            for (int i = 0; i < DL; ++i) a[i] += av[u][i];
+        }
     }
+    for (; c < nch; c += 4) {
+        const float *pc = ph + (int64_t)c * (D + 1);
+        l += pc[D];
+#pragma unroll
+        for (int i = 0; i < DL; ++i) a[i] += pc[lane + 64 * i];
+    }
+#pragma unroll
+    for (int i = 0; i < DL; ++i) sa[w][lane + 64 * i] = a[i];
+    if (lane == 0) sa[w][D] = l;
+    __syncthreads();
+    if (w != 0) return;
+    mall = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
+    l = (sa[0][D] + sa[1][D]) + (sa[2][D] + sa[3][D]);
     const float osc = p.v_scale != nullptr ? p.v_scale[hq / p.G] : 1.f;
     const float inv = osc / l;
     __bf16 *op = (__bf16 *)p.o + (int64_t)s * p.o_st + (int64_t)hq * p.o_sh;
 #pragma unroll
-    for (int i = 0; i < D / 64; ++i) op[lane + 64 * i] = (__bf16)(a[i] * inv);
+    for (int i = 0; i < DL; ++i) {
+        const int d = lane + 64 * i;
+        op[d] = (__bf16)(((sa[0][d] + sa[1][d]) + (sa[2][d] + sa[3][d])) * inv);
+    }
     if (lane == 0 && p.lse != nullptr) p.lse[(int64_t)hq * p.lse_sh + s] = (mall * p.c_log2 + __log2f(l)) * kLn2;
 }
 
@@ -1604,7 +1720,7 @@ bool find_dec(int dtype, int D, bool paged, int G, DecKernels &out) {
     return true;
 }
 
-// Key blocks per chunk: about 2048 (sequence, KV head, chunk) work items.
+// Key blocks per chunk: about 4096 (sequence, KV head, chunk) work items.
 struct DecLayout {
     int64_t J_max, C, n_chunks, s_off, m_off, part_off, bytes;
 };
@@ -1612,11 +1728,15 @@ DecLayout dec_layout(int n_heads_q, int n_heads_kv, int n_seqs, int64_t total_k,
     DecLayout L;
     L.J_max = cdiv(max_k, block_k);
     const int64_t units = (int64_t)n_seqs * n_heads_kv * L.J_max;
-    L.C = units > 2048 ? cdiv(units, 2048) : 1;
+    // about 4096 work items; chunks of whole multiples of 4 blocks (one per wave), at most kDecMaxC
+    L.C = units > 4096 * 4 ? 4 * cdiv(units, 4096 * 4) : 4;
+    if (L.C > kDecMaxC) L.C = kDecMaxC;
     L.n_chunks = L.J_max > 0 ? cdiv(L.J_max, L.C) : 0;
     auto up = [](int64_t x) { return (x + 255) & ~(int64_t)255; };
     L.s_off = 0;
-    L.m_off = up((int64_t)n_heads_q * total_k * 4);
+    const int G = n_heads_q / n_heads_kv;
+    const int GP = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8;
+    L.m_off = up((int64_t)n_heads_kv * total_k * GP * 4);
     L.part_off = L.m_off + up((int64_t)n_heads_q * n_seqs * L.J_max * 4);
     L.bytes = L.part_off + up((int64_t)n_heads_q * n_seqs * L.n_chunks * (head_dim + 1) * 4);
     return L;
@@ -1952,7 +2072,7 @@ bsp_status_t bsp_attn_decode(const bsp_tensor_t *q, const bsp_tensor_t *k, const
         p.part = (float *)(ws + L.part_off);
         hipLaunchKernelGGL(kern.scores, dim3((unsigned)grid), dim3(256), 0, hs, p);
         hipLaunchKernelGGL(kern.pv, dim3((unsigned)grid), dim3(256), 0, hs, p);
-        hipLaunchKernelGGL(kern.combine, dim3((unsigned)((int64_t)n_seqs * n_heads_q)), dim3(64), 0, hs, p);
+        hipLaunchKernelGGL(kern.combine, dim3((unsigned)((int64_t)n_seqs * n_heads_q)), dim3(256), 0, hs, p);
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(BSP_ERR_HIP, "launch failed: %s", hipGetErrorString(e));

@@ -41,7 +41,7 @@ def _one_row_each(inp):
 
 
 @pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("fp8", 128)], ids=["bf16_d128", "bf16_d64", "fp8"])
-@pytest.mark.parametrize("heads", [(8, 2), (6, 2), (4, 4), (16, 2)], ids=["g4", "g3", "g1", "g8"])
+@pytest.mark.parametrize("heads", [(8, 2), (6, 2), (4, 4), (4, 2), (16, 2)], ids=["g4", "g3", "g1", "g2", "g8"])
 @pytest.mark.parametrize("paged", [False, True], ids=["packed", "paged"])
 def test_decode_small_cases(dtype, D, heads, paged):
     hq, hkv = heads
