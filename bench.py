@@ -104,6 +104,60 @@ def time_each(fn, steps, flush=None):
     return float(np.median(out))
 
 
+def decode_rows(bsp, w, q, k, v, scales, dense_lam, finite, steps):
+    """Decoding steps (bsp_attn_decode) after the workload's single sequence: one
+    context at the workload's lambdas (its own keys), and a batch of 16 contexts
+    of the same length on distinct pages of random data at lambda = +inf."""
+    import torch
+
+    H, D = w.n_heads_q, w.head_dim
+    L = int(q.shape[0])
+    # ---- decoding steps (bsp_attn_decode): one new query row per sequence.
+    # Algorithmic HBM bytes: K of every key, V of the blocks some query head of
+    # the KV group keeps (here: of every block for lambda = +inf).
+    dec = []
+    es = k.element_size()
+    kv_row_bytes = w.n_heads_kv * D * es
+    cu1 = torch.tensor([0, L], dtype=torch.int32, device="cuda")
+    q1 = q[L - 1:].contiguous()
+    ws1 = torch.empty(bsp.decode_workspace_bytes(H, w.n_heads_kv, 1, L, L, D, w.block_k), dtype=torch.uint8,
+                      device="cuda")
+    sc1 = torch.empty(H, dtype=torch.int64, device="cuda")
+    vc1 = torch.empty(H, dtype=torch.int64, device="cuda")
+    for lam in [dense_lam] + [x for x in (5.3,) if finite] + finite[-1:]:
+        def fn(lam=lam):
+            return bsp.decode(q1, k, v, cu1, L, block_k=w.block_k, lam=lam, q_scale=scales[0],
+                              k_scale=scales[1], v_scale=scales[2], want_bitmap=False, skip_count=sc1,
+                              visited_count=vc1, workspace=ws1)
+        ms_d = time_calls(fn, steps * 5, 5)
+        f = int(sc1.sum().item()) / max(1, int(vc1.sum().item()))
+        byts = L * kv_row_bytes * (2.0 - f)  # V skipped only where every head of a group skips: an upper bound
+        dec.append({"batch": 1, "lk": L, "lambda": lam, "ms": ms_d, "tokens_per_s": 1.0 / (ms_d * 1e-3),
+                    "skip_fraction": f, "kv_gbs_upper": byts / (ms_d * 1e-3) / 1e9})
+    # a batch of 16 contexts of the same length, distinct pages of random data (lambda = +inf)
+    B, page = 16, 64
+    n_pages = B * L // page
+    kp = torch.randn((n_pages, page, w.n_heads_kv, D), device="cuda").to(k.dtype)
+    vp = torch.randn((n_pages, page, w.n_heads_kv, D), device="cuda").to(k.dtype)
+    table = torch.randperm(n_pages, device="cuda", dtype=torch.int64).to(torch.int32).view(B, L // page).contiguous()
+    cuB = torch.arange(0, (B + 1) * L, L, dtype=torch.int32, device="cuda")
+    qB = torch.randn((B, H, D), device="cuda").to(q.dtype)
+    wsB = torch.empty(bsp.decode_workspace_bytes(H, w.n_heads_kv, B, B * L, L, D, w.block_k), dtype=torch.uint8,
+                      device="cuda")
+
+    def fnB():
+        return bsp.decode(qB, kp, vp, cuB, L, total_k=B * L, block_table=table, block_k=w.block_k, lam=dense_lam,
+                          q_scale=scales[0], k_scale=scales[1], v_scale=scales[2], want_bitmap=False,
+                          workspace=wsB)
+    ms_b = time_calls(fnB, steps * 2, 3)
+    byts = B * L * kv_row_bytes * 2.0
+    dec.append({"batch": B, "lk": L, "lambda": dense_lam, "paged": page, "ms": ms_b, "tokens_per_s": B / (ms_b * 1e-3),
+                "skip_fraction": 0.0, "kv_gbs": byts / (ms_b * 1e-3) / 1e9,
+                "hbm_frac": byts / (ms_b * 1e-3) / 1e9 / HBM_GBS, "data": "random normal (timing only)"})
+    del kp, vp, wsB
+    return dec
+
+
 def cpu_baseline(inp, w, lam, target_s=15.0):
     """Time the CPU oracle on a bounded, deterministic sample of the workload
     and scale its rate to the whole job by visited (tile, block) pairs. The
@@ -164,6 +218,8 @@ def main():
     ap.add_argument("--sparse-steps", type=int, default=10)
     ap.add_argument("--extra-steps", type=int, default=10,
                     help="calls per extra measurement (median/flushed timing, ablation, chunk, decode); 0 skips")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="time only the decoding steps (single-sequence workloads); for kernel traces")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -233,6 +289,13 @@ def main():
     visited = pair_counts(inp.seqlens, w.block_q, w.block_k) * H
     unit_flops = 2.0 * w.block_q * w.block_k * D
     dense_flops = dense_causal_flops(inp.seqlens, H, D)
+
+    if args.decode_only:
+        finite = [x for x in lambdas if not math.isinf(x)]
+        print(json.dumps({"workload": w.name, "dtype": dtype,
+                          "decode": decode_rows(bsp, w, q, k, v, scales, dense_lam, finite, max(1, args.extra_steps))}),
+              flush=True)
+        return
 
     # ---- timed step: dense mode (lambda = +inf)
     ms = time_calls(call(dense_lam), args.steps, args.warmup)
@@ -355,50 +418,7 @@ def main():
                              "kv_gbs": kv_bytes / (ms_c * 1e-3) / 1e9 if lq == 1 else None})
         result["chunked"] = rows
 
-        # ---- decoding steps (bsp_attn_decode): one new query row per sequence.
-        # Algorithmic HBM bytes: K of every key, V of the blocks some query head of
-        # the KV group keeps (here: of every block for lambda = +inf).
-        dec = []
-        es = k.element_size()
-        kv_row_bytes = w.n_heads_kv * D * es
-        cu1 = torch.tensor([0, L], dtype=torch.int32, device="cuda")
-        q1 = q[L - 1:].contiguous()
-        ws1 = torch.empty(bsp.decode_workspace_bytes(H, w.n_heads_kv, 1, L, L, D, w.block_k), dtype=torch.uint8,
-                          device="cuda")
-        sc1 = torch.empty(H, dtype=torch.int64, device="cuda")
-        vc1 = torch.empty(H, dtype=torch.int64, device="cuda")
-        for lam in [dense_lam] + [x for x in (5.3,) if finite] + finite[-1:]:
-            def fn(lam=lam):
-                return bsp.decode(q1, k, v, cu1, L, block_k=w.block_k, lam=lam, q_scale=scales[0],
-                                  k_scale=scales[1], v_scale=scales[2], want_bitmap=False, skip_count=sc1,
-                                  visited_count=vc1, workspace=ws1)
-            ms_d = time_calls(fn, args.extra_steps * 5, 5)
-            f = int(sc1.sum().item()) / max(1, int(vc1.sum().item()))
-            byts = L * kv_row_bytes * (2.0 - f)  # V skipped only where every head of a group skips: an upper bound
-            dec.append({"batch": 1, "lk": L, "lambda": lam, "ms": ms_d, "tokens_per_s": 1.0 / (ms_d * 1e-3),
-                        "skip_fraction": f, "kv_gbs_upper": byts / (ms_d * 1e-3) / 1e9})
-        # a batch of 16 contexts of the same length, distinct pages of random data (lambda = +inf)
-        B, page = 16, 64
-        n_pages = B * L // page
-        kp = torch.randn((n_pages, page, w.n_heads_kv, D), device="cuda").to(k.dtype)
-        vp = torch.randn((n_pages, page, w.n_heads_kv, D), device="cuda").to(k.dtype)
-        table = torch.randperm(n_pages, device="cuda", dtype=torch.int64).to(torch.int32).view(B, L // page).contiguous()
-        cuB = torch.arange(0, (B + 1) * L, L, dtype=torch.int32, device="cuda")
-        qB = torch.randn((B, H, D), device="cuda").to(q.dtype)
-        wsB = torch.empty(bsp.decode_workspace_bytes(H, w.n_heads_kv, B, B * L, L, D, w.block_k), dtype=torch.uint8,
-                          device="cuda")
-
-        def fnB():
-            return bsp.decode(qB, kp, vp, cuB, L, total_k=B * L, block_table=table, block_k=w.block_k, lam=dense_lam,
-                              q_scale=scales[0], k_scale=scales[1], v_scale=scales[2], want_bitmap=False,
-                              workspace=wsB)
-        ms_b = time_calls(fnB, args.extra_steps * 2, 3)
-        byts = B * L * kv_row_bytes * 2.0
-        dec.append({"batch": B, "lk": L, "lambda": dense_lam, "paged": page, "ms": ms_b, "tokens_per_s": B / (ms_b * 1e-3),
-                    "skip_fraction": 0.0, "kv_gbs": byts / (ms_b * 1e-3) / 1e9,
-                    "hbm_frac": byts / (ms_b * 1e-3) / 1e9 / HBM_GBS, "data": "random normal (timing only)"})
-        del kp, vp, wsB
-        result["decode"] = dec
+        result["decode"] = decode_rows(bsp, w, q, k, v, scales, dense_lam, finite, args.extra_steps)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, w, dense_lam, target_s=args.cpu_seconds)
