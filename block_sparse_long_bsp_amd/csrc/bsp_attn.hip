@@ -29,6 +29,7 @@
 
 #include <math.h>
 #include <stdarg.h>
+#include <stddef.h>
 #include <stdint.h>
 #include <stdio.h>
 #include <string.h>
@@ -82,6 +83,18 @@ struct FwdParams {
 };
 
 constexpr float kLn2 = 0.69314718055994530942f;
+
+// Field of the kernel's single by-value argument (at offset 0 of the kernel
+// argument segment), loaded where it is used: a volatile load that the compiler
+// cannot hoist to the kernel entry, so the value does not hold a scalar register
+// through the main loop. (Taking the address of the argument instead would make
+// the compiler copy it to private memory.)
+template <typename T>
+__device__ __forceinline__ T late_kernel_arg(size_t offset) {
+    const auto *seg = (const __attribute__((address_space(4))) char *)__builtin_amdgcn_kernarg_segment_ptr();
+    return *(const volatile __attribute__((address_space(4))) T *)(seg + offset);
+}
+#define BSP_LATE_ARG(S, field) late_kernel_arg<decltype(S::field)>(offsetof(S, field))
 
 #define BSP_LDS(T, ptr) ((__attribute__((address_space(3))) T *)(ptr))
 
@@ -491,6 +504,22 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
     f32x16 sacc[MT];
     float pe[NE];           // probabilities of the current block, element e = 16 mt + i
 
+    // Causal mask of the block at key kb (called only where the block reaches
+    // past this wave's first query): key 32mt + 8(i/4) + 4hh + i%4 of the block
+    // is hidden from query position qpos iff 32mt + 8(i/4) + i%4 > qpos - kb - 4hh.
+    // One compare and select per element, fenced, so that a single lane mask is
+    // live at a time (all 64 masks at once exhaust the scalar registers).
+    auto causal_mask = [&](int kb) {
+        const int d = qpos - kb - 4 * hh;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                sacc[mt][i] = (32 * mt + 8 * (i >> 2) + (i & 3) > d) ? -INFINITY : sacc[mt][i];
+                SCHED_FENCE();
+            }
+    };
+
     // ---- S^T = K_j Q^T : sacc[mt] holds keys 32mt + 8(i/4) + 4hh + i%4 for query qrow;
     // causal mask; returns the row maximum over the block. MFMA f = ks*MT + mt
     // (k-step outermost, so consecutive MFMAs use independent accumulators); its K
@@ -531,15 +560,7 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
                 SCHED_FENCE();
             }
         }
-        if (kb + BK - 1 > off + q0) {  // causal mask (only where the block reaches past this wave's first query)
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int key = kb + 32 * mt + 8 * (i >> 2) + 4 * hh + (i & 3);
-                    if (key > qpos) sacc[mt][i] = -INFINITY;
-                }
-        }
+        if (kb + BK - 1 > off + q0) causal_mask(kb);
         float m = -INFINITY;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) m = max_fold16(m, sacc[mt]);
@@ -699,15 +720,7 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
             constexpr bool CP = decltype(do_copy)::value;
             constexpr int EG = NE / (2 * CI);  // exponentials per copy
             const int kb = j * BK;
-            if (kb + BK - 1 > off + q0) {  // causal mask (only where the block reaches past this wave's first query)
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int key = kb + 32 * mt + 8 * (i >> 2) + 4 * hh + (i & 3);
-                        if (key > qpos) sacc[mt][i] = -INFINITY;
-                    }
-            }
+            if (kb + BK - 1 > off + q0) causal_mask(kb);
             float m = -INFINITY;
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) m = max_fold16(m, sacc[mt]);
@@ -894,10 +907,14 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
     }
     if (pend) pv_block(pprev, sV[F8 ? 0 : ((nblk - 1) & 1)]);
 
-    // ---- epilogue: normalise, store O (bf16) and LSE (natural log)
+    // ---- epilogue: normalise, store O (bf16) and LSE (natural log). The output
+    // fields are read here from the kernel argument segment (BSP_LATE_ARG), so
+    // they are loaded at this point instead of occupying scalar registers
+    // across the loop.
     if (valid) {
         const float inv = osc / l_run;
-        __bf16 *op = (__bf16 *)p.o + (int64_t)(base + qrow) * p.o_st + (int64_t)h * p.o_sh;
+        __bf16 *op = (__bf16 *)BSP_LATE_ARG(FwdParams, o) + (int64_t)(base + qrow) * BSP_LATE_ARG(FwdParams, o_st) +
+                     (int64_t)h * BSP_LATE_ARG(FwdParams, o_sh);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -906,14 +923,17 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
                                   (__bf16)(oacc[dt][4 * g4 + 2] * inv), (__bf16)(oacc[dt][4 * g4 + 3] * inv)};
                 *(bf16x4 *)(op + 32 * dt + 8 * g4 + 4 * hh) = x;
             }
-        if (hh == 0 && p.lse != nullptr)
-            p.lse[(int64_t)h * p.lse_sh + base + qrow] = (m_ref * c + __log2f(l_run)) * kLn2;
+        float *lse = BSP_LATE_ARG(FwdParams, lse);
+        if (hh == 0 && lse != nullptr)
+            lse[(int64_t)h * BSP_LATE_ARG(FwdParams, lse_sh) + base + qrow] = (m_ref * c + __log2f(l_run)) * kLn2;
     }
     if (wq == 0 && lane == 0) {
-        if (p.skip_count) atomicAdd(&p.skip_count[h], (unsigned long long)lg.nskip);
-        if (p.visited_count) atomicAdd(&p.visited_count[h], (unsigned long long)nblk);
-        if (p.seq_skip) atomicAdd(&p.seq_skip[s], (unsigned long long)lg.nskip);
-        if (p.seq_visited) atomicAdd(&p.seq_visited[s], (unsigned long long)nblk);
+        unsigned long long *c0 = BSP_LATE_ARG(FwdParams, skip_count), *c1 = BSP_LATE_ARG(FwdParams, visited_count);
+        unsigned long long *c2 = BSP_LATE_ARG(FwdParams, seq_skip), *c3 = BSP_LATE_ARG(FwdParams, seq_visited);
+        if (c0) atomicAdd(&c0[h], (unsigned long long)lg.nskip);
+        if (c1) atomicAdd(&c1[h], (unsigned long long)nblk);
+        if (c2) atomicAdd(&c2[s], (unsigned long long)lg.nskip);
+        if (c3) atomicAdd(&c3[s], (unsigned long long)nblk);
     }
 }
 
