@@ -284,7 +284,11 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
     constexpr int CI = KBLKB / 1024 / NW;  // copy instructions per wave per block
     constexpr int VROWB = D * 2;     // bytes per LDS row of V (bf16 for both input types)
     constexpr int VBLKB = BK * VROWB;
-    constexpr int NVB = F8 ? 1 : 2;  // bf16 V buffers (fp8: widened in a phase of its own, one buffer)
+    // Ping-pong dense schedule: two query heads of four waves each, so that waves
+    // w and w + 4 (which share a SIMD) belong to different heads.
+    constexpr bool PP = DENSE && HPW == 2 && WPH == 4;
+    // bf16 V buffers (the lockstep fp8 loop widens V in a phase of its own and needs one)
+    constexpr int NVB = (F8 && !PP) ? 1 : 2;
     static_assert(KBLKB % (1024 * NW) == 0, "block copy must split evenly over the waves");
     static_assert(!F8 || D == 128, "fp8 kernels are built for head_dim 128");
     __shared__ __attribute__((aligned(1024))) char sK[2][KBLKB];
@@ -424,7 +428,7 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
     };
     // fp8: widen this wave's own staged V bytes (its copies of the block, landed
     // once vmcnt says so) into the bf16 V buffer, in the bf16 row swizzle.
-    auto widen_v = [&]() {
+    auto widen_v = [&](char *vdst) {
         if constexpr (F8) {
 #pragma unroll
             for (int i = 0; i < CI; ++i) {
@@ -435,7 +439,7 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
                                   fp8x2_to_bf16x2<false>(x[1]), fp8x2_to_bf16x2<true>(x[1])};
                 const u32x4 hi = {fp8x2_to_bf16x2<false>(x[2]), fp8x2_to_bf16x2<true>(x[2]),
                                   fp8x2_to_bf16x2<false>(x[3]), fp8x2_to_bf16x2<true>(x[3])};
-                char *row = sV[0] + r * VROWB;
+                char *row = vdst + r * VROWB;
                 *(u32x4 *)(row + (((2 * c16) ^ chunk_swz<D>(r)) << 4)) = lo;
                 *(u32x4 *)(row + (((2 * c16 + 1) ^ chunk_swz<D>(r)) << 4)) = hi;
             }
@@ -645,9 +649,6 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
         return rs0 + rs1;
     };
 
-    // Ping-pong dense schedule: bf16, two query heads of four waves each, so
-    // that waves w and w + 4 (which share a SIMD) belong to different heads.
-    constexpr bool PP = DENSE && !F8 && HPW == 2 && WPH == 4;
 
     if constexpr (PP) {
         // ---- dense ping-pong. Per block j every wave runs a matrix phase
@@ -665,7 +666,12 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
         // M_{j-1}) ran in interval 2j - 1.
         auto issue_copy = [&](int j, int i) {  // copy i of this wave's share (K first, then V)
             if (i < CI) copy_one(kg, kstb, (j + 1) * BK, sK[(j + 1) & 1], true, i);
+            else if constexpr (F8) copy_one(vg, vstb, j * BK, sV8, false, i - CI);  // fp8 V: staged, widened later
             else copy_one(vg, vstb, j * BK, sV[j & 1], true, i - CI);
+        };
+        // fp8: once its copies of V_j have landed, each wave widens them into the bf16 buffer of block j
+        auto land_v = [&](int j) {
+            if constexpr (F8) widen_v(sV[j & 1]);
         };
         // M phase: PV_{j-1} (probabilities pprev, V_{j-1} in LDS) and then QK_j
         // (K_j in LDS -> sacc). Only one wave of the SIMD issues matrix work in
@@ -684,25 +690,41 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
             static_assert(!CP || NS % (2 * CI) == 0, "copies must spread evenly over the matrix phase");
             const char *kbuf = sK[j & 1];
             const char *vbuf = sV[(j - 1) & 1];
-            auto opread = [&](int x) -> bf16x8 {
-                if (x < P0) return vread_at(vbuf, x / DT, x % DT);
-                const int f = x - P0, ks = f / MT, mt = f % MT;
-                return *(const bf16x8 *)(kbuf + krow + 32 * mt * KROWB + (((2 * ks + hh) ^ ksw) << 4));
+            typedef typename std::conditional<F8, i32x8, bf16x8>::type KOp;
+            bf16x8 vop[NS];  // V operands of the PV slots
+            KOp kop[NS];     // K operands of the QK slots (fp8: 64 dims of a row per lane half)
+            auto opread = [&](int x) {
+                if (x < P0) {
+                    vop[x] = vread_at(vbuf, x / DT, x % DT);
+                } else {
+                    const int f = x - P0, ks = f / MT, mt = f % MT;
+                    const char *rowp = kbuf + krow + 32 * mt * KROWB;
+                    if constexpr (F8) {
+                        const u32x4 lo = *(const u32x4 *)(rowp + (((4 * ks + 2 * hh) ^ ksw) << 4));
+                        const u32x4 hi = *(const u32x4 *)(rowp + (((4 * ks + 2 * hh + 1) ^ ksw) << 4));
+                        kop[x] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                       (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+                    } else {
+                        kop[x] = *(const bf16x8 *)(rowp + (((2 * ks + hh) ^ ksw) << 4));
+                    }
+                }
             };
             // This wave's MFMAs issue ahead of its SIMD partner's vector work.
             __builtin_amdgcn_s_setprio(1);
-            bf16x8 op[NS];
 #pragma unroll
-            for (int x = 0; x < PD && x < NS; ++x) op[x] = opread(x);
+            for (int x = 0; x < PD && x < NS; ++x) opread(x);
 #pragma unroll
             for (int x = 0; x < NS; ++x) {
-                if (x + PD < NS) op[x + PD] = opread(x + PD);
+                if (x + PD < NS) opread(x + PD);
                 if (x < P0) {
-                    oacc[x % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[x], pprev[x / DT], oacc[x % DT], 0, 0, 0);
+                    oacc[x % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[x], pprev[x / DT], oacc[x % DT], 0, 0, 0);
                 } else {
                     const int f = x - P0;
-                    sacc[f % MT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[x], qf[f / MT],
-                                                                           f < MT ? f32x16{} : sacc[f % MT], 0, 0, 0);
+                    const f32x16 c0 = f < MT ? f32x16{} : sacc[f % MT];
+                    if constexpr (F8)
+                        sacc[f % MT] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kop[x], qf[f / MT], c0, 0, 0, 0, 0, 0, 0);
+                    else
+                        sacc[f % MT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[x], qf[f / MT], c0, 0, 0, 0);
                 }
                 if constexpr (CP) {
                     if (x % CSLOT == 0) {
@@ -754,12 +776,14 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
             __syncthreads();
             v_phase(0, F_{}, 0);                          // interval 1
             wait_vmem_all();
+            land_v(0);
             __syncthreads();
             for (int j = 1; j < n; ++j) {
                 m_phase(j, T_{}, T_{}, T_{});             // interval 2j
                 __syncthreads();
                 v_phase(j, F_{}, 0);                      // interval 2j + 1
                 wait_vmem_all();
+                land_v(j);
                 __syncthreads();
             }
             m_phase(n, T_{}, F_{}, F_{});                 // interval 2n: PV_{n-1}
@@ -769,12 +793,14 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
             __syncthreads();
             m_phase(0, F_{}, T_{}, F_{});                 // interval 1
             wait_vmem_all();
+            land_v(0);
             __syncthreads();
             for (int j = 1; j < n; ++j) {
                 v_phase(j - 1, T_{}, j);                  // interval 2j (copies of K_{j+1}, V_j)
                 __syncthreads();
                 m_phase(j, T_{}, T_{}, F_{});             // interval 2j + 1
                 wait_vmem_all();
+                land_v(j);
                 __syncthreads();
             }
             v_phase(n - 1, F_{}, 0);                      // interval 2n
@@ -808,7 +834,7 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
             const float mloc = qk_phase(j);
             // V_{j-1} must be in LDS before B1; K_{j+1} may still fly.
             wait_vmem_leave<CI>();
-            widen_v();
+            widen_v(sV[0]);
             __syncthreads();  // B1
             if constexpr (F8) copy_block(vg, vstb, j * BK, sV8, false);
             else copy_block(vg, vstb, j * BK, sV[cur], true);
@@ -837,7 +863,7 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
             // V_{j-1} (copied during the previous block) must be in LDS before B1; K_{j+1} may still fly.
             if (v_prev) {
                 wait_vmem_leave<CI>();
-                widen_v();
+                widen_v(sV[0]);
             }
             __syncthreads();  // B1: votes and V_{j-1} visible; every wave is done with QK_j
             bool skip = false;
@@ -902,7 +928,7 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
     }
     wait_vmem_all();  // also the copy past the last K block, before the workgroup ends
     if (v_prev) {
-        widen_v();
+        widen_v(sV[0]);
         __syncthreads();
     }
     if (pend) pv_block(pprev, sV[F8 ? 0 : ((nblk - 1) & 1)]);
