@@ -80,6 +80,9 @@ struct FwdParams {
     const float *lam_seq;           // lambda per sequence, or NULL
     unsigned long long *seq_skip, *seq_visited;  // counts per sequence, or NULL
     uint32_t flags;                 // BSP_FLAG_* ablation switches
+    // dense mode run with other blocks than the caller's (results do not depend on
+    // them at lambda = +inf): visited counts in the caller's (block_q, block_k); 0: the kernel's
+    int32_t acct_bq, acct_bk;
 };
 
 constexpr float kLn2 = 0.69314718055994530942f;
@@ -957,9 +960,14 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
         unsigned long long *c0 = BSP_LATE_ARG(FwdParams, skip_count), *c1 = BSP_LATE_ARG(FwdParams, visited_count);
         unsigned long long *c2 = BSP_LATE_ARG(FwdParams, seq_skip), *c3 = BSP_LATE_ARG(FwdParams, seq_visited);
         if (c0) atomicAdd(&c0[h], (unsigned long long)lg.nskip);
-        if (c1) atomicAdd(&c1[h], (unsigned long long)nblk);
+        int vis = nblk;
+        if (p.acct_bq > 0) {  // the caller's query tiles inside this one, each with its causal key blocks
+            vis = 0;
+            for (int r0 = t * BQ; r0 < r1; r0 += p.acct_bq) vis += (off + min(r0 + p.acct_bq, L) - 1) / p.acct_bk + 1;
+        }
+        if (c1) atomicAdd(&c1[h], (unsigned long long)vis);
         if (c2) atomicAdd(&c2[s], (unsigned long long)lg.nskip);
-        if (c3) atomicAdd(&c3[s], (unsigned long long)nblk);
+        if (c3) atomicAdd(&c3[s], (unsigned long long)vis);
     }
 }
 
@@ -1901,14 +1909,26 @@ bsp_status_t bsp_attn_fwd_ex(const bsp_tensor_t *q, const bsp_tensor_t *k, const
             return fail(BSP_ERR_UNSUPPORTED, "k/v token stride too large (max(block_k, page_size) * stride must stay below 2 GiB)");
     }
     const int hpw = heads_per_workgroup(q->dtype, n_heads_q / n_heads_kv);
-    const int64_t grid64 = T_max * (int64_t)seqs->n_seqs * (n_heads_q / hpw);
-    if (grid64 > 0x7fffffffLL) return fail(BSP_ERR_INVALID_ARG, "too many work items");
     // dense-mode kernel: lambda = +inf for every sequence (no vote, nothing to ablate)
     const bool dense = isinf(lambda) && opts->lambda_per_seq == nullptr;
     kernel_fn fn = find_kernel(q->dtype, head_dim, block_q, block_k, paged, hpw, dense);
     if (fn == nullptr)
         return fail(BSP_ERR_UNSUPPORTED, "no kernel for dtype %d, head_dim %d, block_q %d, block_k %d", (int)q->dtype,
                     head_dim, block_q, block_k);
+    // Dense mode decides nothing, so O and LSE do not depend on the block sizes (up to
+    // rounding order) and the bitmap stays zero: run the 128 x 128 instance (the
+    // fastest schedule) and count visited blocks in the caller's units.
+    int kbq = block_q, kbk = block_k;
+    if (dense && q->dtype != BSP_F32 && (block_q != 128 || block_k != 128) && 128 % block_q == 0) {
+        kernel_fn f128 = find_kernel(q->dtype, head_dim, 128, 128, paged, hpw, true);
+        if (f128 != nullptr) {
+            fn = f128;
+            kbq = kbk = 128;
+        }
+    }
+    const int64_t T_launch = cdiv(seqs->max_seqlen, kbq);
+    const int64_t grid64 = T_launch * (int64_t)seqs->n_seqs * (n_heads_q / hpw);
+    if (grid64 > 0x7fffffffLL) return fail(BSP_ERR_INVALID_ARG, "too many work items");
 
     // ---------------- device
     if ((st = check_device()) != BSP_OK) return st;
@@ -1949,7 +1969,7 @@ bsp_status_t bsp_attn_fwd_ex(const bsp_tensor_t *q, const bsp_tensor_t *k, const
         p.skip_count = c0;
         p.visited_count = c1;
         p.n_seqs = seqs->n_seqs;
-        p.T_max = (int32_t)T_max;
+        p.T_max = (int32_t)T_launch;  // tiles of the launched kernel (the bitmap is not written in dense mode)
         p.W = (int32_t)W;
         p.Hq = n_heads_q;
         p.Hkv = n_heads_kv;
@@ -1969,7 +1989,9 @@ bsp_status_t bsp_attn_fwd_ex(const bsp_tensor_t *q, const bsp_tensor_t *k, const
         p.seq_skip = c2;
         p.seq_visited = c3;
         p.flags = opts->flags;
-        hipLaunchKernelGGL(fn, dim3((unsigned)grid64), dim3(block_q * 2 * hpw), 0, hs, p);
+        p.acct_bq = (kbq != block_q || kbk != block_k) ? block_q : 0;
+        p.acct_bk = (kbq != block_q || kbk != block_k) ? block_k : 0;
+        hipLaunchKernelGGL(fn, dim3((unsigned)grid64), dim3(kbq * 2 * hpw), 0, hs, p);
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(BSP_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
