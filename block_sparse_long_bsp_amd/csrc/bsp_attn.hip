@@ -1315,10 +1315,27 @@ __global__ void __launch_bounds__(256) dec_scores(DecParams p) {
     constexpr int RPW = 64 / LPR;
     static_assert(LPR == 8 || LPR == 16, "a row is 8 or 16 lanes");
     int s, g, c, kbase, Lk, nblk, j0, j1;
-    if (!dec_item(p, s, g, c, kbase, Lk, nblk, j0, j1)) return;
+    const bool work = dec_item(p, s, g, c, kbase, Lk, nblk, j0, j1);
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int sub = lane % LPR, rw = lane / LPR;
     const int G = p.G;
+    if (c == 0) {
+        // outputs of this (sequence, KV head), before any early exit: its bitmap rows, the
+        // query heads' counts (by sequence 0) and the sequence's counts (by KV head 0).
+        // dec_pv, the next kernel, then adds to them.
+        if (p.bitmap != nullptr)
+            for (int i = tid; i < G * p.W; i += 256)
+                p.bitmap[((int64_t)(g * G + i / p.W) * p.n_seqs + s) * p.W + i % p.W] = 0u;
+        if (s == 0 && tid < G) {
+            if (p.skip_count) p.skip_count[g * G + tid] = 0ull;
+            if (p.visited_count) p.visited_count[g * G + tid] = 0ull;
+        }
+        if (g == 0 && tid == 0) {
+            if (p.seq_skip) p.seq_skip[s] = 0ull;
+            if (p.seq_visited) p.seq_visited[s] = 0ull;
+        }
+    }
+    if (!work) return;
+    const int sub = lane % LPR, rw = lane / LPR;
     constexpr int NPR = EPL / 2;  // bf16 pairs per lane per row
     bf16x2 qp[GP][NPR];
     float sqk[GP];
@@ -1383,6 +1400,68 @@ __global__ void __launch_bounds__(256) dec_scores(DecParams p) {
             p.M[((int64_t)(g * G + lane) * p.n_seqs + s) * p.J_max + j] = m;
         }
     }
+}
+
+// o and lse of one (sequence, query head) from the chunk partials: four waves
+// (the whole workgroup) take every fourth chunk, lanes take dimensions, then
+// wave 0 adds up and stores.
+template <int D>
+__device__ __forceinline__ void dec_combine_head(const DecParams &p, int s, int hq, int nblk) {
+    constexpr int DL = D / 64;  // dimensions per lane
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    __shared__ float sm[4];
+    __shared__ float sa[4][D + 1];
+    const float *Mh = p.M + ((int64_t)hq * p.n_seqs + s) * p.J_max;
+    float mall = -INFINITY;
+    for (int j = tid; j < nblk; j += 256) mall = fmaxf(mall, Mh[j]);
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) mall = fmaxf(mall, __shfl_xor(mall, m));
+    if (lane == 0) sm[w] = mall;
+    const int nch = (nblk + p.C - 1) / p.C;
+    const float *ph = p.part + ((int64_t)hq * p.n_seqs + s) * p.n_chunks * (D + 1);
+    float l = 0.f;
+    float a[DL] = {};
+    int c = w;
+    for (; c + 12 < nch; c += 16) {  // four chunks of this wave in flight
+        float lv[4], av[4][DL];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float *pc = ph + (int64_t)(c + 4 * u) * (D + 1);
+            lv[u] = pc[D];
+#pragma unroll
+            for (int i = 0; i < DL; ++i) av[u][i] = pc[lane + 64 * i];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            l += lv[u];
+#pragma unroll
+            for (int i = 0; i < DL; ++i) a[i] += av[u][i];
+        }
+    }
+    for (; c < nch; c += 4) {
+        const float *pc = ph + (int64_t)c * (D + 1);
+        l += pc[D];
+#pragma unroll
+        for (int i = 0; i < DL; ++i) a[i] += pc[lane + 64 * i];
+    }
+#pragma unroll
+    for (int i = 0; i < DL; ++i) sa[w][lane + 64 * i] = a[i];
+    if (lane == 0) sa[w][D] = l;
+    __syncthreads();
+    if (w == 0) {
+        mall = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
+        l = (sa[0][D] + sa[1][D]) + (sa[2][D] + sa[3][D]);
+        const float osc = p.v_scale != nullptr ? p.v_scale[hq / p.G] : 1.f;
+        const float inv = osc / l;
+        __bf16 *op = (__bf16 *)p.o + (int64_t)s * p.o_st + (int64_t)hq * p.o_sh;
+#pragma unroll
+        for (int i = 0; i < DL; ++i) {
+            const int d = lane + 64 * i;
+            op[d] = (__bf16)(((sa[0][d] + sa[1][d]) + (sa[2][d] + sa[3][d])) * inv);
+        }
+        if (lane == 0 && p.lse != nullptr) p.lse[(int64_t)hq * p.lse_sh + s] = (mall * p.c_log2 + __log2f(l)) * kLn2;
+    }
+    __syncthreads();  // sm / sa are reused by the next call
 }
 
 // Decisions, probabilities and the partial PV of one chunk.
@@ -1569,68 +1648,18 @@ __global__ void __launch_bounds__(256) dec_pv(DecParams p) {
     }
 }
 
-// o and lse of one (sequence, query head) from the chunk partials: four waves
-// take every fourth chunk, lanes take dimensions, then the waves add up.
+// o and lse from the chunk partials, one workgroup per (sequence, query head).
+// (A combine by the last chunk's workgroup, behind an arrival counter, needs a
+// device-scope fence in every workgroup; on this GPU that writes back the L2
+// and made the step slower than a separate launch.)
 template <int D>
 __global__ void __launch_bounds__(256) dec_combine(DecParams p) {
-    constexpr int DL = D / 64;  // dimensions per lane
     const int hq = blockIdx.x % p.Hq, s = blockIdx.x / p.Hq;
     const int kbase = p.cu_k[s];
     const int Lk = p.cu_k[s + 1] - kbase;
     const int nblk = Lk > 0 ? min((Lk + p.BK - 1) / p.BK, p.J_max) : 0;
     if (nblk == 0) return;  // a sequence without keys: nothing written
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    __shared__ float sm[4];
-    __shared__ float sa[4][D + 1];
-    const float *Mh = p.M + ((int64_t)hq * p.n_seqs + s) * p.J_max;
-    float mall = -INFINITY;
-    for (int j = tid; j < nblk; j += 256) mall = fmaxf(mall, Mh[j]);
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) mall = fmaxf(mall, __shfl_xor(mall, m));
-    if (lane == 0) sm[w] = mall;
-    const int nch = (nblk + p.C - 1) / p.C;
-    const float *ph = p.part + ((int64_t)hq * p.n_seqs + s) * p.n_chunks * (D + 1);
-    float l = 0.f;
-    float a[DL] = {};
-    int c = w;
-    for (; c + 12 < nch; c += 16) {  // four chunks of this wave in flight
-        float lv[4], av[4][DL];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const float *pc = ph + (int64_t)(c + 4 * u) * (D + 1);
-            lv[u] = pc[D];
-#pragma unroll
-            for (int i = 0; i < DL; ++i) av[u][i] = pc[lane + 64 * i];
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            l += lv[u];
-#pragma unroll
-            for (int i = 0; i < DL; ++i) a[i] += av[u][i];
-        }
-    }
-    for (; c < nch; c += 4) {
-        const float *pc = ph + (int64_t)c * (D + 1);
-        l += pc[D];
-#pragma unroll
-        for (int i = 0; i < DL; ++i) a[i] += pc[lane + 64 * i];
-    }
-#pragma unroll
-    for (int i = 0; i < DL; ++i) sa[w][lane + 64 * i] = a[i];
-    if (lane == 0) sa[w][D] = l;
-    __syncthreads();
-    if (w != 0) return;
-    mall = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
-    l = (sa[0][D] + sa[1][D]) + (sa[2][D] + sa[3][D]);
-    const float osc = p.v_scale != nullptr ? p.v_scale[hq / p.G] : 1.f;
-    const float inv = osc / l;
-    __bf16 *op = (__bf16 *)p.o + (int64_t)s * p.o_st + (int64_t)hq * p.o_sh;
-#pragma unroll
-    for (int i = 0; i < DL; ++i) {
-        const int d = lane + 64 * i;
-        op[d] = (__bf16)(((sa[0][d] + sa[1][d]) + (sa[2][d] + sa[3][d])) * inv);
-    }
-    if (lane == 0 && p.lse != nullptr) p.lse[(int64_t)hq * p.lse_sh + s] = (mall * p.c_log2 + __log2f(l)) * kLn2;
+    dec_combine_head<D>(p, s, hq, nblk);
 }
 
 // Zero the bitmap and the counters ahead of the main kernel (a plain fill
@@ -2082,7 +2111,8 @@ bsp_status_t bsp_attn_decode(const bsp_tensor_t *q, const bsp_tensor_t *k, const
     unsigned long long *c1 = skip_out ? skip_out->visited_count : nullptr;
     unsigned long long *c2 = opts->skip_count_per_seq;
     unsigned long long *c3 = opts->visited_count_per_seq;
-    if (bitmap != nullptr || c0 != nullptr || c1 != nullptr || c2 != nullptr || c3 != nullptr) {
+    // (with work to do, dec_scores zeroes the bitmap and the counts itself)
+    if (grid == 0 && (bitmap != nullptr || c0 != nullptr || c1 != nullptr || c2 != nullptr || c3 != nullptr)) {
         int64_t work = words > n_heads_q ? words : n_heads_q;
         if (work < n_seqs) work = n_seqs;
         const int blocks = (int)(cdiv(work, 256) < 1024 ? cdiv(work, 256) : 1024);

@@ -228,8 +228,8 @@ int64_t bsp_skip_bitmap_words_kv(int n_heads_q, int n_seqs, int max_seqlen_q, in
  *            overwritten. Concurrent calls need separate workspaces.
  * Supported: bf16 head_dim 64 or 128, fp8 e4m3 head_dim 128, up to 8 query
  * heads per KV head (else BSP_ERR_UNSUPPORTED). A sequence with Lk = 0 gets no
- * output. The call is asynchronous on `stream` (three kernels plus the output
- * fill) and allocates nothing.
+ * output. The call is asynchronous on `stream` (three kernels) and
+ * allocates nothing.
  */
 typedef struct {
     const float *lambda_per_seq;                /* device float[n_seqs] or NULL */

@@ -231,7 +231,8 @@ def test_decode_workspace_bytes(lib):
     chunks = 64  # groups of 4 blocks (one per wave): 1 x 8 x 64 work items
     assert n == 8 * 32768 * 4 * 4 + 32 * J * 4 + 32 * chunks * 129 * 4
     # three query heads per KV head store their scores padded to four
-    assert bsp.decode_workspace_bytes(24, 8, 1, 4096, 4096, 128, 128) == 8 * 4096 * 4 * 4 + 24 * 32 * 4 + 24 * 8 * 129 * 4
+    assert bsp.decode_workspace_bytes(24, 8, 1, 4096, 4096, 128, 128) == (8 * 4096 * 4 * 4 + 24 * 32 * 4
+                                                                           + 24 * 8 * 129 * 4)
     # many sequences: blocks are grouped so that about 2048 work items remain
     n16 = bsp.decode_workspace_bytes(32, 8, 16, 16 * 20000, 32768, 128, 128)
     assert n16 >= 32 * 16 * 20000 * 4 + 32 * 16 * 256 * 4
