@@ -289,9 +289,12 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
     constexpr int VBLKB = BK * VROWB;
     // Ping-pong dense schedule: two query heads of four waves each, so that waves
     // w and w + 4 (which share a SIMD) belong to different heads.
+    // Sparse mode runs the same schedule with a vote after QK (SPP), except the
+    // fp8 paged instance, which would not fit the registers.
     constexpr bool PP = DENSE && HPW == 2 && WPH == 4;
+    constexpr bool SPP = !DENSE && HPW == 2 && WPH == 4 && !(F8 && PAGED);
     // bf16 V buffers (the lockstep fp8 loop widens V in a phase of its own and needs one)
-    constexpr int NVB = (F8 && !PP) ? 1 : 2;
+    constexpr int NVB = (F8 && !PP && !SPP) ? 1 : 2;
     static_assert(KBLKB % (1024 * NW) == 0, "block copy must split evenly over the waves");
     static_assert(!F8 || D == 128, "fp8 kernels are built for head_dim 128");
     __shared__ __attribute__((aligned(1024))) char sK[2][KBLKB];
@@ -653,8 +656,8 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
     };
 
 
-    if constexpr (PP) {
-        // ---- dense ping-pong. Per block j every wave runs a matrix phase
+    if constexpr (PP || SPP) {
+        // ---- ping-pong. Per block j every wave runs a matrix phase
         // M_j = PV_{j-1} + QK_j and a vector phase V_j (mask, max, reference,
         // exponentials, row sum, bf16 probabilities). Head 1 runs half a block
         // behind head 0, the two separated by workgroup barriers: while head 0
@@ -771,10 +774,161 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
             }
             finish_block(rs0 + rs1, alpha, resc);
         };
+
+        // ---- sparse mode on the same schedule. The matrix phase is split into a
+        // PV part, run only if this head kept block j - 1, with its own operand
+        // prologue (so the branch around it leaves one register assignment), and
+        // a QK part that also carries the interval's copies and ends with this
+        // wave's vote on block j (causal mask, row max, every valid row's gap to
+        // the running max above lambda). The barrier after the matrix phase
+        // publishes the votes; the vector phase reads the head's four votes,
+        // records the decision, and for a kept block runs the reference update,
+        // exponentials and row sum. V_j is copied before any head has decided,
+        // so this schedule loads V for skipped blocks too.
+        float mloc_cur = -INFINITY;
+        auto pv_part = [&](int j) {  // PV_{j-1}
+            constexpr int PD = kPingPongDepth;
+            const char *vbuf = sV[(j - 1) & 1];
+            bf16x8 vop[NPV];
+            __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+            for (int x = 0; x < PD && x < NPV; ++x) vop[x] = vread_at(vbuf, x / DT, x % DT);
+#pragma unroll
+            for (int x = 0; x < NPV; ++x) {
+                if (x + PD < NPV) vop[x + PD] = vread_at(vbuf, (x + PD) / DT, (x + PD) % DT);
+                oacc[x % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[x], pprev[x / DT], oacc[x % DT], 0, 0, 0);
+                SCHED_FENCE();
+            }
+            __builtin_amdgcn_s_setprio(0);
+        };
+        auto qk_vote = [&](int j, auto do_copy) {  // QK_j, this interval's copies (if this wave issues them), vote
+            constexpr bool CP = decltype(do_copy)::value;
+            constexpr int NQK = KS * MT;
+            constexpr int PD = kPingPongDepth;
+            constexpr int CSLOT = NQK / (2 * CI);
+            static_assert(!CP || NQK % (2 * CI) == 0, "copies must spread evenly over the QK MFMAs");
+            const char *kbuf = sK[j & 1];
+            typedef typename std::conditional<F8, i32x8, bf16x8>::type KOp;
+            KOp kop[NQK];
+            auto kread = [&](int f) {
+                const int ks = f / MT, mt = f % MT;
+                const char *rowp = kbuf + krow + 32 * mt * KROWB;
+                if constexpr (F8) {
+                    const u32x4 lo = *(const u32x4 *)(rowp + (((4 * ks + 2 * hh) ^ ksw) << 4));
+                    const u32x4 hi = *(const u32x4 *)(rowp + (((4 * ks + 2 * hh + 1) ^ ksw) << 4));
+                    kop[f] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                   (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+                } else {
+                    kop[f] = *(const bf16x8 *)(rowp + (((2 * ks + hh) ^ ksw) << 4));
+                }
+            };
+            __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+            for (int f = 0; f < PD && f < NQK; ++f) kread(f);
+#pragma unroll
+            for (int f = 0; f < NQK; ++f) {
+                if (f + PD < NQK) kread(f + PD);
+                const f32x16 c0 = f < MT ? f32x16{} : sacc[f % MT];
+                if constexpr (F8)
+                    sacc[f % MT] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kop[f], qf[f / MT], c0, 0, 0, 0, 0, 0, 0);
+                else
+                    sacc[f % MT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[f], qf[f / MT], c0, 0, 0, 0);
+                if constexpr (CP) {
+                    if (f % CSLOT == 0) {
+                        SCHED_FENCE();
+                        issue_copy(j, f / CSLOT);
+                    }
+                }
+                SCHED_FENCE();
+            }
+            __builtin_amdgcn_s_setprio(0);
+            const int kb = j * BK;
+            if (kb + BK - 1 > off + q0) causal_mask(kb);
+            float m = -INFINITY;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) m = max_fold16(m, sacc[mt]);
+            mloc_cur = fmaxf(m, __shfl_xor(m, 32));
+            const bool ok = !valid || (mloc_cur == -INFINITY) || (m_dec - mloc_cur > lam_raw);
+            const int wall = __all(ok);
+            if (lane == 0) sVote[w] = wall;
+        };
+        // Vector phase of block j in sparse mode. It takes the exponentials of a
+        // skipped block too (a branch around them costs the instance its registers):
+        // against the unchanged reference, since the block's maximum is left out of
+        // the running max, and then drops them (no row sum into l, pend stays false).
+        // So BSP_FLAG_EXP_SKIPPED changes nothing on this schedule.
+        auto v_sparse = [&](int j, auto do_copy, int cj) {
+            constexpr bool CP = decltype(do_copy)::value;
+            constexpr int EG = NE / (2 * CI);
+            int vall = 1;
+#pragma unroll
+            for (int y = 0; y < WPH; ++y) vall &= (sVote[hl * WPH + y] != 0) ? 1 : 0;
+            const bool sk = __builtin_amdgcn_readfirstlane(vall) != 0;
+            if (wq == 0) log_decision(p, lg, bm_row, j, nblk, sk, lane == 0);
+            pend = !sk;
+            float alpha, rs0 = 0.f, rs1 = 0.f;
+            bool resc;
+            const float mc = new_reference(sk ? -INFINITY : mloc_cur, alpha, resc);
+#pragma unroll
+            for (int e = 0; e < NE; ++e) {
+                pe[e] = __builtin_amdgcn_exp2f(fmaf(sacc[e >> 4][e & 15], c, -mc));
+                if (e & 1) {
+                    rs0 += pe[e - 1];
+                    rs1 += pe[e];
+                }
+                if constexpr (CP) {
+                    if (e % EG == EG - 1) {
+                        SCHED_FENCE();
+                        issue_copy(cj, e / EG);
+                        SCHED_FENCE();
+                    }
+                }
+            }
+            finish_block(sk ? 0.f : rs0 + rs1, alpha, resc);
+        };
+
         using T_ = std::true_type;
         using F_ = std::false_type;
         const int n = nblk;
-        if (hl == 0) {
+        if constexpr (SPP) {
+            if (hl == 0) {
+                qk_vote(0, T_{});                         // interval 0
+                __syncthreads();
+                v_sparse(0, F_{}, 0);                     // interval 1
+                wait_vmem_all();
+                land_v(0);
+                __syncthreads();
+                for (int j = 1; j < n; ++j) {
+                    if (pend) pv_part(j);                 // interval 2j
+                    qk_vote(j, T_{});
+                    __syncthreads();
+                    v_sparse(j, F_{}, 0);                 // interval 2j + 1
+                    wait_vmem_all();
+                    land_v(j);
+                    __syncthreads();
+                }
+                if (pend) pv_part(n);                     // interval 2n
+            } else {
+#pragma unroll
+                for (int i = 0; i < 2 * CI; ++i) issue_copy(0, i);  // interval 0: K_1, V_0
+                __syncthreads();
+                qk_vote(0, F_{});                         // interval 1
+                wait_vmem_all();
+                land_v(0);
+                __syncthreads();
+                for (int j = 1; j < n; ++j) {
+                    v_sparse(j - 1, T_{}, j);             // interval 2j (copies of K_{j+1}, V_j)
+                    __syncthreads();
+                    if (pend) pv_part(j);                 // interval 2j + 1
+                    qk_vote(j, F_{});
+                    wait_vmem_all();
+                    land_v(j);
+                    __syncthreads();
+                }
+                v_sparse(n - 1, F_{}, 0);                 // interval 2n
+                if (pend) pv_part(n);                     // interval 2n + 1
+            }
+        } else if (hl == 0) {
             m_phase(0, F_{}, T_{}, T_{});                 // interval 0
             __syncthreads();
             v_phase(0, F_{}, 0);                          // interval 1
