@@ -852,39 +852,58 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
             const int wall = __all(ok);
             if (lane == 0) sVote[w] = wall;
         };
-        // Vector phase of block j in sparse mode. It takes the exponentials of a
-        // skipped block too (a branch around them costs the instance its registers):
-        // against the unchanged reference, since the block's maximum is left out of
-        // the running max, and then drops them (no row sum into l, pend stays false).
-        // So BSP_FLAG_EXP_SKIPPED changes nothing on this schedule.
+        // Vector phase of block j in sparse mode: the head's decision, then, for a
+        // kept block, the reference update, exponentials (in place in the score
+        // registers), row sum and bf16 probabilities. A skipped block zeroes the
+        // probabilities instead, so that they are dead from a PV part to the next
+        // vector phase on both paths (else they stay live through QK next to the
+        // scores). The interval's copies, when this wave issues them here, go
+        // first: interleaved with the exponentials they cost the instance its
+        // registers. Ablation (BSP_FLAG_EXP_SKIPPED): a skipped block's
+        // exponentials are taken on the kept path against the unchanged reference
+        // (its maximum is left out of the running max) and dropped.
         auto v_sparse = [&](int j, auto do_copy, int cj) {
             constexpr bool CP = decltype(do_copy)::value;
-            constexpr int EG = NE / (2 * CI);
             int vall = 1;
 #pragma unroll
             for (int y = 0; y < WPH; ++y) vall &= (sVote[hl * WPH + y] != 0) ? 1 : 0;
             const bool sk = __builtin_amdgcn_readfirstlane(vall) != 0;
             if (wq == 0) log_decision(p, lg, bm_row, j, nblk, sk, lane == 0);
             pend = !sk;
-            float alpha, rs0 = 0.f, rs1 = 0.f;
-            bool resc;
-            const float mc = new_reference(sk ? -INFINITY : mloc_cur, alpha, resc);
+            if constexpr (CP) {
 #pragma unroll
-            for (int e = 0; e < NE; ++e) {
-                pe[e] = __builtin_amdgcn_exp2f(fmaf(sacc[e >> 4][e & 15], c, -mc));
-                if (e & 1) {
-                    rs0 += pe[e - 1];
-                    rs1 += pe[e];
-                }
-                if constexpr (CP) {
-                    if (e % EG == EG - 1) {
-                        SCHED_FENCE();
-                        issue_copy(cj, e / EG);
-                        SCHED_FENCE();
+                for (int i = 0; i < 2 * CI; ++i) issue_copy(cj, i);
+            }
+            if (!sk || (p.flags & BSP_FLAG_EXP_SKIPPED) != 0) {
+                float alpha, rs0 = 0.f, rs1 = 0.f;
+                bool resc;
+                const float mc = new_reference(sk ? -INFINITY : mloc_cur, alpha, resc);
+#pragma unroll
+                for (int e = 0; e < NE; ++e) {
+                    sacc[e >> 4][e & 15] = __builtin_amdgcn_exp2f(fmaf(sacc[e >> 4][e & 15], c, -mc));
+                    if (e & 1) {
+                        rs0 += sacc[(e - 1) >> 4][(e - 1) & 15];
+                        rs1 += sacc[e >> 4][e & 15];
                     }
                 }
+                float rs = sk ? 0.f : rs0 + rs1;
+                rs += __shfl_xor(rs, 32);
+                if (resc) {
+                    l_run *= alpha;
+#pragma unroll
+                    for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+                }
+                l_run += rs;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int u = 0; u < 2; ++u)
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) pprev[2 * mt + u][i] = (__bf16)sacc[mt][8 * u + i];
+            } else {
+#pragma unroll
+                for (int cc = 0; cc < PC; ++cc) pprev[cc] = bf16x8{};
             }
-            finish_block(sk ? 0.f : rs0 + rs1, alpha, resc);
         };
 
         using T_ = std::true_type;

@@ -245,13 +245,14 @@ def test_repeat_runs_are_bit_identical():
             assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("block_q,block_k", [(64, 64), (128, 128)])
-def test_gqa_equals_repeated_kv_mha(block_q, block_k):
-    """Sharing a KV head among 4 query heads gives what 4 copies of it give.
+@pytest.mark.parametrize("block,hq,exact", [(64, 4, True), (64, 8, True), (128, 8, False)],
+                         ids=["64_g2", "64_g4", "128_g4"])
+def test_gqa_equals_repeated_kv_mha(block, hq, exact):
+    """Sharing a KV head among the query heads of a group gives what copies of it give.
 
-    At block_q = 64 both calls run the same loop and must agree bit for bit. At
-    block_q = 128 the GQA call pairs two heads per workgroup on the two-head
-    schedule and the MHA call runs one head per workgroup, which sums the row
+    At 64 x 64 both calls run the lockstep loop (two heads and one head per
+    workgroup) and must agree bit for bit. At 128 x 128 the GQA call runs the
+    two-head schedule and the MHA call the one-head loop, which sums the row
     sums in another order: the decisions (exact maxima of the same scores) must
     still agree bit for bit, O and LSE to rounding.
     """
@@ -259,17 +260,17 @@ def test_gqa_equals_repeated_kv_mha(block_q, block_k):
 
     import block_sparse_long_bsp_amd as bsp
 
-    # sink and vertical-line structure: the oracle skips 73 (64 x 64) and 7 (128 x 128) blocks
-    # at lambda 1.5, no gap within 0.02 of it
-    inp = synth.build_inputs((333,), 8, 2, 128, "bf16", rho=0.97, n_vert=3, code=205, sink_gain=6.0)
+    # sink and vertical-line structure: the oracle skips blocks in every case at lambda 1.5
+    # (group 2 at 64: 38 of 84; group 4 at 64: 73 of 168, at 128: 7 of 48), no gap within 0.02 of it
+    inp = synth.build_inputs((333,), hq, 2, 128, "bf16", rho=0.97, n_vert=3, code=205, sink_gain=6.0)
     dev = parity.to_device(inp)
-    a = bsp.fwd(dev["q"], dev["k"], dev["v"], dev["cu"], inp.max_seqlen, block_q=block_q, block_k=block_k, lam=1.5)
-    k4 = dev["k"].repeat_interleave(4, dim=1).contiguous()
-    v4 = dev["v"].repeat_interleave(4, dim=1).contiguous()
-    b = bsp.fwd(dev["q"], k4, v4, dev["cu"], inp.max_seqlen, block_q=block_q, block_k=block_k, lam=1.5)
+    a = bsp.fwd(dev["q"], dev["k"], dev["v"], dev["cu"], inp.max_seqlen, block_q=block, block_k=block, lam=1.5)
+    kr = dev["k"].repeat_interleave(hq // 2, dim=1).contiguous()
+    vr = dev["v"].repeat_interleave(hq // 2, dim=1).contiguous()
+    b = bsp.fwd(dev["q"], kr, vr, dev["cu"], inp.max_seqlen, block_q=block, block_k=block, lam=1.5)
     torch.cuda.synchronize()
     assert int(a[3].sum()) > 0  # some blocks skipped
-    if block_q == 64:
+    if exact:
         for x, y in zip(a, b):
             assert torch.equal(x, y)
         return
