@@ -162,7 +162,10 @@ int64_t bsp_skip_bitmap_words(int n_heads_q, int n_seqs, int max_seqlen, int blo
  *     settings, section 5, step 3): BSP_FLAG_LOAD_SKIPPED_V copies V also for
  *     blocks that every query head of the workgroup skips; BSP_FLAG_EXP_SKIPPED
  *     computes (and discards) the exponentials of skipped blocks. Results are
- *     unchanged; only the work done changes.
+ *     unchanged; only the work done changes. Kernels whose schedule issues the
+ *     V copy of a block before its decision (bf16, and fp8 with packed K/V,
+ *     with an even GQA group at block_q 128) load every V block anyway, so
+ *     BSP_FLAG_LOAD_SKIPPED_V changes nothing for them.
  */
 #define BSP_FLAG_LOAD_SKIPPED_V 1u
 #define BSP_FLAG_EXP_SKIPPED 2u
