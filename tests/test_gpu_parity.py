@@ -196,28 +196,38 @@ def test_chunk8k_of_llama8b_32k_sampled():
 # ---- lambda per sequence, counts per sequence, ablation switches --
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp8", "f32"])
-def test_lambda_per_sequence(dtype):
+@pytest.mark.parametrize("block", [64, 128])
+def test_lambda_per_sequence(dtype, block):
+    # block 128 (bf16, fp8): the two-head ping-pong schedule in sparse mode; the oracle skips
+    # 6 of 100 pairs there
+    if dtype == "f32" and block == 128:
+        pytest.skip("the fp32 kernel is built for 64 x 64 blocks at head_dim 64")
     D = 64 if dtype == "f32" else 128
     seqs = (300, 129, 77, 513)
     inp = synth.build_inputs(seqs, 4, 2, D, dtype, rho=0.95, n_vert=2, code=213, sink_gain=6.0)
-    bq, bk = (64, 64)
-    _log(f"lambda per sequence dtype={dtype}")
+    bq = bk = block
+    _log(f"lambda per sequence dtype={dtype} block={bq}")
     reps = parity.check_case(inp, bq, bk, [7.0], lam_seq=[0.0, math.inf, 2.0, 0.5])
     assert reps[0].n_skipped > 0
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp8", "f32"])
-def test_ablation_flags_leave_results_unchanged(dtype):
+@pytest.mark.parametrize("block", [64, 128])
+def test_ablation_flags_leave_results_unchanged(dtype, block):
+    # block 128 (bf16, fp8): the two-head ping-pong schedule, where the exponential switch sends
+    # skipped blocks down the kept path; the oracle skips 20 (bf16) and 21 (fp8) of 96 pairs there
     import torch
 
     import block_sparse_long_bsp_amd as bsp
 
+    if dtype == "f32" and block == 128:
+        pytest.skip("the fp32 kernel is built for 64 x 64 blocks at head_dim 64")
     D = 64 if dtype == "f32" else 128
     inp = synth.build_inputs((700, 129), 4, 2, D, dtype, rho=0.97, n_vert=2, code=214, sink_gain=6.0)
     dev = parity.to_device(inp)
     outs = []
     for flags in (0, bsp.FLAG_LOAD_SKIPPED_V, bsp.FLAG_EXP_SKIPPED, bsp.FLAG_LOAD_SKIPPED_V | bsp.FLAG_EXP_SKIPPED):
-        r = bsp.fwd(dev["q"], dev["k"], dev["v"], dev["cu"], inp.max_seqlen, block_q=64, block_k=64, lam=1.0,
+        r = bsp.fwd(dev["q"], dev["k"], dev["v"], dev["cu"], inp.max_seqlen, block_q=block, block_k=block, lam=1.0,
                     q_scale=dev["q_scale"], k_scale=dev["k_scale"], v_scale=dev["v_scale"], flags=flags)
         torch.cuda.synchronize()
         outs.append([x.clone() for x in r])
