@@ -83,6 +83,10 @@ struct FwdParams {
     // dense mode run with other blocks than the caller's (results do not depend on
     // them at lambda = +inf): visited counts in the caller's (block_q, block_k); 0: the kernel's
     int32_t acct_bq, acct_bk;
+    // sparse mode at block_q = 64 run on a 128-row tile: each 64-row half of the
+    // tile takes its own decisions (the caller's tiles), 0: one decision per tile
+    int32_t half_vote;
+    int32_t T_bm;                   // bitmap tiles per (head, sequence) row: the caller's block_q
 };
 
 constexpr float kLn2 = 0.69314718055994530942f;
@@ -327,8 +331,23 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
     const int qrow = q0 + ln;
     const bool valid = qrow < L;
     const int qpos = off + qrow;       // key position of this lane's query
-    const int64_t bm_row = ((int64_t)h * p.n_seqs + s) * p.T_max + t;
     constexpr bool dense = DENSE;  // lambda = +inf: every block is kept, no vote
+    // Decisions this wave records on the two-head sparse schedule: nlog blocks of
+    // bitmap tile tb (0 for a wave that records nothing). One tile-wide decision:
+    // wave 0 of each head records all visited blocks of the tile. Half-tile votes
+    // (the caller's block_q is 64): waves 0 and 2 record the causal blocks of
+    // their 64-row half, tile 2t or 2t + 1 in the caller's units.
+    int tb = t, nlog = nblk;
+    if constexpr (SPP) {
+        if (p.half_vote != 0) {
+            tb = 2 * t + (wq >> 1);
+            const int r0 = tb * (BQ / 2);
+            nlog = ((wq & 1) == 0 && r0 < L) ? (off + min(r0 + BQ / 2, L) - 1) / BK + 1 : 0;
+        } else if (wq != 0) {
+            nlog = 0;
+        }
+    }
+    const int64_t bm_row = ((int64_t)h * p.n_seqs + s) * p.T_bm + tb;
     float c = p.c_log2;           // raw score -> base-2 exponent
     float lam_raw = p.lam_raw;    // lambda in raw score units
     float osc = 1.f;              // output scale
@@ -864,11 +883,14 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
         // (its maximum is left out of the running max) and dropped.
         auto v_sparse = [&](int j, auto do_copy, int cj) {
             constexpr bool CP = decltype(do_copy)::value;
+            // the votes of this wave's head, or of its half-tile's two waves
+            const int vmask = p.half_vote != 0 ? 3 << (wq & 2) : (1 << WPH) - 1;
             int vall = 1;
 #pragma unroll
-            for (int y = 0; y < WPH; ++y) vall &= (sVote[hl * WPH + y] != 0) ? 1 : 0;
+            for (int y = 0; y < WPH; ++y)
+                if ((vmask >> y) & 1) vall &= (sVote[hl * WPH + y] != 0) ? 1 : 0;
             const bool sk = __builtin_amdgcn_readfirstlane(vall) != 0;
-            if (wq == 0) log_decision(p, lg, bm_row, j, nblk, sk, lane == 0);
+            if (j < nlog) log_decision(p, lg, bm_row, j, nlog, sk, lane == 0);
             pend = !sk;
             if constexpr (CP) {
 #pragma unroll
@@ -1129,6 +1151,13 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
         if (hh == 0 && lse != nullptr)
             lse[(int64_t)h * BSP_LATE_ARG(FwdParams, lse_sh) + base + qrow] = (m_ref * c + __log2f(l_run)) * kLn2;
     }
+    // wave 0 of the head adds the tile's visited blocks; the waves that recorded
+    // decisions add their skips (wave 2 as well under half-tile votes)
+    if (SPP && lane == 0 && wq == 2 && BSP_LATE_ARG(FwdParams, half_vote) != 0 && lg.nskip != 0) {
+        unsigned long long *c0 = BSP_LATE_ARG(FwdParams, skip_count), *c2 = BSP_LATE_ARG(FwdParams, seq_skip);
+        if (c0) atomicAdd(&c0[h], (unsigned long long)lg.nskip);
+        if (c2) atomicAdd(&c2[s], (unsigned long long)lg.nskip);
+    }
     if (wq == 0 && lane == 0) {
         unsigned long long *c0 = BSP_LATE_ARG(FwdParams, skip_count), *c1 = BSP_LATE_ARG(FwdParams, visited_count);
         unsigned long long *c2 = BSP_LATE_ARG(FwdParams, seq_skip), *c3 = BSP_LATE_ARG(FwdParams, seq_visited);
@@ -1182,7 +1211,7 @@ __global__ void __launch_bounds__(BQ * 2) fwd_f32(FwdParams p) {
     const int qrow = q0 + ln;
     const bool valid = qrow < L;
     const int qpos = off + qrow;
-    const int64_t bm_row = ((int64_t)h * p.n_seqs + s) * p.T_max + t;
+    const int64_t bm_row = ((int64_t)h * p.n_seqs + s) * p.T_bm + t;
     const float lam_raw = p.lam_seq == nullptr ? p.lam_raw
                           : (p.lam_seq[s] == INFINITY ? INFINITY : p.lam_seq[s] / p.scale);
 
@@ -2128,6 +2157,18 @@ bsp_status_t bsp_attn_fwd_ex(const bsp_tensor_t *q, const bsp_tensor_t *k, const
             kbq = kbk = 128;
         }
     }
+    // Sparse mode at block_q = 64: the 128 x block_k instance runs the two-head
+    // ping-pong schedule, and each 64-row half of its tile votes on its own, so the
+    // decisions, the bitmap and the counts stay those of the caller's 64-row tiles.
+    int half_vote = 0;
+    if (!dense && q->dtype != BSP_F32 && block_q == 64 && hpw == 2 && !(q->dtype == BSP_FP8_E4M3 && paged)) {
+        kernel_fn f128 = find_kernel(q->dtype, head_dim, 128, block_k, paged, hpw, false);
+        if (f128 != nullptr) {
+            fn = f128;
+            kbq = 128;
+            half_vote = 1;
+        }
+    }
     const int64_t T_launch = cdiv(seqs->max_seqlen, kbq);
     const int64_t grid64 = T_launch * (int64_t)seqs->n_seqs * (n_heads_q / hpw);
     if (grid64 > 0x7fffffffLL) return fail(BSP_ERR_INVALID_ARG, "too many work items");
@@ -2171,7 +2212,9 @@ bsp_status_t bsp_attn_fwd_ex(const bsp_tensor_t *q, const bsp_tensor_t *k, const
         p.skip_count = c0;
         p.visited_count = c1;
         p.n_seqs = seqs->n_seqs;
-        p.T_max = (int32_t)T_launch;  // tiles of the launched kernel (the bitmap is not written in dense mode)
+        p.T_max = (int32_t)T_launch;  // tiles of the launched kernel
+        p.T_bm = (int32_t)T_max;      // bitmap tiles: the caller's (dense mode writes no bitmap)
+        p.half_vote = half_vote;
         p.W = (int32_t)W;
         p.Hq = n_heads_q;
         p.Hkv = n_heads_kv;
@@ -2191,6 +2234,7 @@ bsp_status_t bsp_attn_fwd_ex(const bsp_tensor_t *q, const bsp_tensor_t *k, const
         p.seq_skip = c2;
         p.seq_visited = c3;
         p.flags = opts->flags;
+        // counts in the caller's blocks when the launched tile differs from them
         p.acct_bq = (kbq != block_q || kbk != block_k) ? block_q : 0;
         p.acct_bk = (kbq != block_q || kbk != block_k) ? block_k : 0;
         hipLaunchKernelGGL(fn, dim3((unsigned)grid64), dim3(kbq * 2 * hpw), 0, hs, p);

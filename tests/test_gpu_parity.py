@@ -198,8 +198,8 @@ def test_chunk8k_of_llama8b_32k_sampled():
 @pytest.mark.parametrize("dtype", ["bf16", "fp8", "f32"])
 @pytest.mark.parametrize("block", [64, 128])
 def test_lambda_per_sequence(dtype, block):
-    # block 128 (bf16, fp8): the two-head ping-pong schedule in sparse mode; the oracle skips
-    # 6 of 100 pairs there
+    # bf16 and fp8 (group 2): the two-head ping-pong schedule in sparse mode, at block 64 on
+    # 128-row tiles whose halves vote apart; the oracle skips 6 of 100 pairs at block 128
     if dtype == "f32" and block == 128:
         pytest.skip("the fp32 kernel is built for 64 x 64 blocks at head_dim 64")
     D = 64 if dtype == "f32" else 128
@@ -214,8 +214,9 @@ def test_lambda_per_sequence(dtype, block):
 @pytest.mark.parametrize("dtype", ["bf16", "fp8", "f32"])
 @pytest.mark.parametrize("block", [64, 128])
 def test_ablation_flags_leave_results_unchanged(dtype, block):
-    # block 128 (bf16, fp8): the two-head ping-pong schedule, where the exponential switch sends
-    # skipped blocks down the kept path; the oracle skips 20 (bf16) and 21 (fp8) of 96 pairs there
+    # bf16 and fp8 (group 2): the two-head ping-pong schedule (at block 64 on 128-row tiles whose
+    # halves vote apart), where the exponential switch sends skipped blocks down the kept path;
+    # the oracle skips 20 (bf16) and 21 (fp8) of 96 pairs at block 128
     import torch
 
     import block_sparse_long_bsp_amd as bsp
@@ -255,16 +256,17 @@ def test_repeat_runs_are_bit_identical():
             assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("block,hq,exact", [(64, 4, True), (64, 8, True), (128, 8, False)],
-                         ids=["64_g2", "64_g4", "128_g4"])
+@pytest.mark.parametrize("block,hq,exact", [(64, 6, True), (64, 4, False), (64, 8, False), (128, 8, False)],
+                         ids=["64_g3", "64_g2", "64_g4", "128_g4"])
 def test_gqa_equals_repeated_kv_mha(block, hq, exact):
     """Sharing a KV head among the query heads of a group gives what copies of it give.
 
-    At 64 x 64 both calls run the lockstep loop (two heads and one head per
-    workgroup) and must agree bit for bit. At 128 x 128 the GQA call runs the
-    two-head schedule and the MHA call the one-head loop, which sums the row
-    sums in another order: the decisions (exact maxima of the same scores) must
-    still agree bit for bit, O and LSE to rounding.
+    With an odd group at 64 x 64 both calls run the one-head lockstep loop and
+    must agree bit for bit. With an even group the GQA call runs the two-head
+    schedule (at 64 x 64 on 128-row tiles whose 64-row halves vote apart) and
+    the MHA call the one-head loop, which sums the row sums in another order:
+    the decisions (exact maxima of the same scores) must still agree bit for
+    bit, O and LSE to rounding.
     """
     import torch
 
