@@ -274,7 +274,10 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t x) {
     return __builtin_bit_cast(uint32_t, y);
 }
 
-template <int IN, int D, int BQ, int BK, bool PAGED, int HPW, bool DENSE>
+// KH: sparse mode for a caller's 64-key blocks on 128-key blocks. Each 64-key
+// half of a block is decided on its own, in key order, and under half-tile votes
+// (FwdParams::half_vote) each 64-row half of the tile as well.
+template <int IN, int D, int BQ, int BK, bool PAGED, int HPW, bool DENSE, bool KH = false>
 __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) fwd_mfma(FwdParams p) {
     constexpr bool F8 = IN == BSP_FP8_E4M3;
     constexpr int WPH = BQ / 32;     // waves per head
@@ -300,6 +303,7 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
     // bf16 V buffers (the lockstep fp8 loop widens V in a phase of its own and needs one)
     constexpr int NVB = (F8 && !PP && !SPP) ? 1 : 2;
     static_assert(KBLKB % (1024 * NW) == 0, "block copy must split evenly over the waves");
+    static_assert(!KH || (SPP && BK == 128), "key-half votes run on the two-head sparse schedule at 128-key blocks");
     static_assert(!F8 || D == 128, "fp8 kernels are built for head_dim 128");
     __shared__ __attribute__((aligned(1024))) char sK[2][KBLKB];
     __shared__ __attribute__((aligned(1024))) char sV[NVB][VBLKB];
@@ -337,14 +341,16 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
     // wave 0 of each head records all visited blocks of the tile. Half-tile votes
     // (the caller's block_q is 64): waves 0 and 2 record the causal blocks of
     // their 64-row half, tile 2t or 2t + 1 in the caller's units.
+    // Key-half votes (the caller's block_k is 64): nlog counts the caller's blocks.
     int tb = t, nlog = nblk;
     if constexpr (SPP) {
-        if (p.half_vote != 0) {
+        constexpr int cbk = KH ? BK / 2 : BK;
+        if (KH && p.half_vote != 0) {
             tb = 2 * t + (wq >> 1);
             const int r0 = tb * (BQ / 2);
-            nlog = ((wq & 1) == 0 && r0 < L) ? (off + min(r0 + BQ / 2, L) - 1) / BK + 1 : 0;
-        } else if (wq != 0) {
-            nlog = 0;
+            nlog = ((wq & 1) == 0 && r0 < L) ? (off + min(r0 + BQ / 2, L) - 1) / cbk + 1 : 0;
+        } else {
+            nlog = wq == 0 ? (off + r1 - 1) / cbk + 1 : 0;
         }
     }
     const int64_t bm_row = ((int64_t)h * p.n_seqs + s) * p.T_bm + tb;
@@ -804,7 +810,7 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
         // records the decision, and for a kept block runs the reference update,
         // exponentials and row sum. V_j is copied before any head has decided,
         // so this schedule loads V for skipped blocks too.
-        float mloc_cur = -INFINITY;
+        float mloc_a = -INFINITY, mloc_b = -INFINITY;  // row maxima of the block's two key halves
         auto pv_part = [&](int j) {  // PV_{j-1}
             constexpr int PD = kPingPongDepth;
             const char *vbuf = sV[(j - 1) & 1];
@@ -863,13 +869,32 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
             __builtin_amdgcn_s_setprio(0);
             const int kb = j * BK;
             if (kb + BK - 1 > off + q0) causal_mask(kb);
-            float m = -INFINITY;
+            // every valid row's gap from running max mr to block max ml exceeds lambda
+            auto passes = [&](float mr, float ml) { return !valid || ml == -INFINITY || mr - ml > lam_raw; };
+            int vote;
+            if constexpr (KH) {
+                // row maxima of the two key halves (keys 0..BK/2-1 sit in tiles mt < MT/2);
+                // bit 0: first half; bits 1 and 2: second half if the first is skipped / kept
+                float ma = -INFINITY, mb = -INFINITY;
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) m = max_fold16(m, sacc[mt]);
-            mloc_cur = fmaxf(m, __shfl_xor(m, 32));
-            const bool ok = !valid || (mloc_cur == -INFINITY) || (m_dec - mloc_cur > lam_raw);
-            const int wall = __all(ok);
-            if (lane == 0) sVote[w] = wall;
+                for (int mt = 0; mt < MT; ++mt) {
+                    if (mt < MT / 2) ma = max_fold16(ma, sacc[mt]);
+                    else mb = max_fold16(mb, sacc[mt]);
+                }
+                mloc_a = fmaxf(ma, __shfl_xor(ma, 32));
+                mloc_b = fmaxf(mb, __shfl_xor(mb, 32));
+                vote = (__all(passes(m_dec, mloc_a)) ? 1 : 0) | (__all(passes(m_dec, mloc_b)) ? 2 : 0) |
+                       (__all(passes(fmaxf(m_dec, mloc_a), mloc_b)) ? 4 : 0);
+            } else {
+                // one decision per block: its maximum stands in the first half's slot
+                float m = -INFINITY;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) m = max_fold16(m, sacc[mt]);
+                mloc_a = fmaxf(m, __shfl_xor(m, 32));
+                mloc_b = -INFINITY;
+                vote = __all(passes(m_dec, mloc_a)) ? 1 : 0;
+            }
+            if (lane == 0) sVote[w] = vote;
         };
         // Vector phase of block j in sparse mode: the head's decision, then, for a
         // kept block, the reference update, exponentials (in place in the score
@@ -879,18 +904,30 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
         // scores). The interval's copies, when this wave issues them here, go
         // first: interleaved with the exponentials they cost the instance its
         // registers. Ablation (BSP_FLAG_EXP_SKIPPED): a skipped block's
-        // exponentials are taken on the kept path against the unchanged reference
-        // (its maximum is left out of the running max) and dropped.
+        // exponentials are taken on the kept path against +inf (its maximum is
+        // left out of the running max), so they come out zero and are dropped.
+        // Under key-half votes a block whose halves are decided apart runs the
+        // kept path, the skipped half's exponentials again taken against +inf.
         auto v_sparse = [&](int j, auto do_copy, int cj) {
             constexpr bool CP = decltype(do_copy)::value;
             // the votes of this wave's head, or of its half-tile's two waves
-            const int vmask = p.half_vote != 0 ? 3 << (wq & 2) : (1 << WPH) - 1;
-            int vall = 1;
+            const int vmask = (KH && p.half_vote != 0) ? 3 << (wq & 2) : (1 << WPH) - 1;
+            int vall = 7;
 #pragma unroll
             for (int y = 0; y < WPH; ++y)
-                if ((vmask >> y) & 1) vall &= (sVote[hl * WPH + y] != 0) ? 1 : 0;
-            const bool sk = __builtin_amdgcn_readfirstlane(vall) != 0;
-            if (j < nlog) log_decision(p, lg, bm_row, j, nlog, sk, lane == 0);
+                if ((vmask >> y) & 1) vall &= sVote[hl * WPH + y];
+            vall = __builtin_amdgcn_readfirstlane(vall);
+            bool ska, skb;  // decisions on the two key halves
+            if constexpr (KH) {
+                ska = (vall & 1) != 0;
+                skb = ((ska ? vall >> 1 : vall >> 2) & 1) != 0;
+                if (2 * j < nlog) log_decision(p, lg, bm_row, 2 * j, nlog, ska, lane == 0);
+                if (2 * j + 1 < nlog) log_decision(p, lg, bm_row, 2 * j + 1, nlog, skb, lane == 0);
+            } else {
+                ska = skb = (vall & 1) != 0;
+                if (j < nlog) log_decision(p, lg, bm_row, j, nlog, ska, lane == 0);
+            }
+            const bool sk = ska && skb;
             pend = !sk;
             if constexpr (CP) {
 #pragma unroll
@@ -899,16 +936,19 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
             if (!sk || (p.flags & BSP_FLAG_EXP_SKIPPED) != 0) {
                 float alpha, rs0 = 0.f, rs1 = 0.f;
                 bool resc;
-                const float mc = new_reference(sk ? -INFINITY : mloc_cur, alpha, resc);
+                const float mc = new_reference(fmaxf(ska ? -INFINITY : mloc_a, skb ? -INFINITY : mloc_b), alpha, resc);
+                // a skipped half's exponentials are taken against +inf: zero probabilities, zero sum
+                const float mca = ska ? INFINITY : mc, mcb = skb ? INFINITY : mc;
 #pragma unroll
                 for (int e = 0; e < NE; ++e) {
-                    sacc[e >> 4][e & 15] = __builtin_amdgcn_exp2f(fmaf(sacc[e >> 4][e & 15], c, -mc));
+                    const float mce = (e >> 4) < MT / 2 ? mca : mcb;
+                    sacc[e >> 4][e & 15] = __builtin_amdgcn_exp2f(fmaf(sacc[e >> 4][e & 15], c, -mce));
                     if (e & 1) {
                         rs0 += sacc[(e - 1) >> 4][(e - 1) & 15];
                         rs1 += sacc[e >> 4][e & 15];
                     }
                 }
-                float rs = sk ? 0.f : rs0 + rs1;
+                float rs = rs0 + rs1;
                 rs += __shfl_xor(rs, 32);
                 if (resc) {
                     l_run *= alpha;
@@ -1153,7 +1193,7 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
     }
     // wave 0 of the head adds the tile's visited blocks; the waves that recorded
     // decisions add their skips (wave 2 as well under half-tile votes)
-    if (SPP && lane == 0 && wq == 2 && BSP_LATE_ARG(FwdParams, half_vote) != 0 && lg.nskip != 0) {
+    if (KH && lane == 0 && wq == 2 && BSP_LATE_ARG(FwdParams, half_vote) != 0 && lg.nskip != 0) {
         unsigned long long *c0 = BSP_LATE_ARG(FwdParams, skip_count), *c2 = BSP_LATE_ARG(FwdParams, seq_skip);
         if (c0) atomicAdd(&c0[h], (unsigned long long)lg.nskip);
         if (c2) atomicAdd(&c2[s], (unsigned long long)lg.nskip);
@@ -1937,6 +1977,19 @@ kernel_fn pick_kernel(int dtype, bool paged, int hpw, bool dense) {
     return nullptr;
 }
 
+// Sparse mode for 64-key blocks (any block_q) on the two-head schedule at 128 x 128
+// (bf16; fp8 with packed K/V, where that schedule fits the registers).
+template <int IN, int D>
+kernel_fn key_half_kernel(bool paged) {
+    return paged ? fwd_mfma<IN, D, 128, 128, true, 2, false, true> : fwd_mfma<IN, D, 128, 128, false, 2, false, true>;
+}
+kernel_fn find_key_half_kernel(int dtype, int D, bool paged) {
+    if (dtype == BSP_BF16 && D == 128) return key_half_kernel<BSP_BF16, 128>(paged);
+    if (dtype == BSP_BF16 && D == 64) return key_half_kernel<BSP_BF16, 64>(paged);
+    if (dtype == BSP_FP8_E4M3 && D == 128 && !paged) return fwd_mfma<BSP_FP8_E4M3, 128, 128, 128, false, 2, false, true>;
+    return nullptr;
+}
+
 // Query heads per workgroup: the bf16 and fp8 kernels pair the query heads of
 // a KV head when the group size is even.
 int heads_per_workgroup(int dtype, int group) { return (dtype != BSP_F32 && group % 2 == 0) ? 2 : 1; }
@@ -2132,13 +2185,6 @@ bsp_status_t bsp_attn_fwd_ex(const bsp_tensor_t *q, const bsp_tensor_t *k, const
             return fail(BSP_ERR_INVALID_ARG, "bitmap holds %lld words, %lld needed", (long long)skip_out->bitmap_words,
                         (long long)words);
     }
-    // K/V copies address rows with 32-bit byte offsets from the first row of a block or a page.
-    {
-        const int64_t es = elem_size(q->dtype);
-        const int64_t rows = paged && bt->page_size > block_k ? bt->page_size : block_k;
-        if (rows * k->stride_token * es >= (1LL << 31) || rows * v->stride_token * es >= (1LL << 31))
-            return fail(BSP_ERR_UNSUPPORTED, "k/v token stride too large (max(block_k, page_size) * stride must stay below 2 GiB)");
-    }
     const int hpw = heads_per_workgroup(q->dtype, n_heads_q / n_heads_kv);
     // dense-mode kernel: lambda = +inf for every sequence (no vote, nothing to ablate)
     const bool dense = isinf(lambda) && opts->lambda_per_seq == nullptr;
@@ -2157,17 +2203,25 @@ bsp_status_t bsp_attn_fwd_ex(const bsp_tensor_t *q, const bsp_tensor_t *k, const
             kbq = kbk = 128;
         }
     }
-    // Sparse mode at block_q = 64: the 128 x block_k instance runs the two-head
-    // ping-pong schedule, and each 64-row half of its tile votes on its own, so the
-    // decisions, the bitmap and the counts stay those of the caller's 64-row tiles.
+    // Sparse mode at 64-row tiles or 64-key blocks: the 128 x 128 instance runs the
+    // two-head ping-pong schedule, each 64-row half of its tile votes on its own
+    // and each 64-key half of its block is decided on its own, so the decisions,
+    // the bitmap and the counts stay those of the caller's blocks.
     int half_vote = 0;
-    if (!dense && q->dtype != BSP_F32 && block_q == 64 && hpw == 2 && !(q->dtype == BSP_FP8_E4M3 && paged)) {
-        kernel_fn f128 = find_kernel(q->dtype, head_dim, 128, block_k, paged, hpw, false);
-        if (f128 != nullptr) {
-            fn = f128;
-            kbq = 128;
-            half_vote = 1;
+    if (!dense && block_k == 64 && hpw == 2) {
+        kernel_fn fkh = find_key_half_kernel(q->dtype, head_dim, paged);
+        if (fkh != nullptr) {
+            fn = fkh;
+            half_vote = block_q == 64 ? 1 : 0;
+            kbq = kbk = 128;
         }
+    }
+    // K/V copies address rows with 32-bit byte offsets from the first row of a block or a page.
+    {
+        const int64_t es = elem_size(q->dtype);
+        const int64_t rows = paged && bt->page_size > kbk ? bt->page_size : kbk;
+        if (rows * k->stride_token * es >= (1LL << 31) || rows * v->stride_token * es >= (1LL << 31))
+            return fail(BSP_ERR_UNSUPPORTED, "k/v token stride too large (max(block_k, page_size) * stride must stay below 2 GiB)");
     }
     const int64_t T_launch = cdiv(seqs->max_seqlen, kbq);
     const int64_t grid64 = T_launch * (int64_t)seqs->n_seqs * (n_heads_q / hpw);
