@@ -164,8 +164,14 @@ int64_t bsp_skip_bitmap_words(int n_heads_q, int n_seqs, int max_seqlen, int blo
  *     computes (and discards) the exponentials of skipped blocks. Results are
  *     unchanged; only the work done changes. Kernels whose schedule issues the
  *     V copy of a block before its decision (bf16, and fp8 with packed K/V,
- *     with an even GQA group at block_q 128) load every V block anyway, so
- *     BSP_FLAG_LOAD_SKIPPED_V changes nothing for them.
+ *     with an even GQA group, at any of the block sizes above) load every V
+ *     block anyway, so BSP_FLAG_LOAD_SKIPPED_V changes nothing for them.
+ *   Those calls run on 128-row tiles and 128-key blocks whatever block_q and
+ *   block_k are. Each 64-row half of a tile and each 64-key half of a block is
+ *   then decided on its own, in key order, so the decisions, the bitmap and
+ *   the counts are those of the caller's blocks. When one 64-key half of a
+ *   128-key block is kept and the other skipped, the kernel still spends the
+ *   whole block's PV and exponentials; the skipped half adds zero.
  */
 #define BSP_FLAG_LOAD_SKIPPED_V 1u
 #define BSP_FLAG_EXP_SKIPPED 2u
