@@ -57,6 +57,36 @@ def test_small_cases(dtype, inst, paged):
     assert reps[2].n_skipped > 0
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("block_q", [64, 128])
+@pytest.mark.parametrize("paged", [False, True], ids=["packed", "paged"])
+def test_key_halves_decided_apart(dtype, block_q, paged):
+    """64-key blocks on 128-key blocks: the two halves of a block take their own decisions.
+
+    The oracle's decisions on these inputs hold, among pairs of 64-key blocks
+    (2i, 2i + 1) that a tile visits, both a kept block followed by a skipped one
+    and a skipped block followed by a kept one, so the second half's vote is
+    exercised both with and without the first half's maximum in the running
+    max. The GPU bitmap must equal the oracle's (outside the decision band),
+    with the counts. (fp8 with paged K/V runs the lockstep loop instead.)
+    """
+    import oracle
+
+    inp = synth.build_inputs((700, 300, 129, 64), 4, 2, 128, dtype, rho=0.95, n_vert=2, code=215, sink_gain=6.0,
+                             paged=paged, page_size=64)
+    ref = oracle.run_inputs(inp, block_q, 64, 1.0, j_max=(inp.max_seqlen + 63) // 64)
+    sk, vis = ref.skip.astype(bool), ref.visited.astype(bool)
+    J = sk.shape[1] // 2 * 2
+    both = vis[:, 0:J:2] & vis[:, 1:J:2]
+    kept_then_skipped = int((both & ~sk[:, 0:J:2] & sk[:, 1:J:2]).sum())
+    skipped_then_kept = int((both & sk[:, 0:J:2] & ~sk[:, 1:J:2]).sum())
+    assert kept_then_skipped > 0 and skipped_then_kept > 0
+    _log(f"key halves dtype={dtype} bq={block_q} paged={paged}: {kept_then_skipped} kept/skipped, "
+         f"{skipped_then_kept} skipped/kept pairs")
+    reps = parity.check_case(inp, block_q, 64, [2.0, 1.0], paged=paged)
+    assert reps[1].n_skipped > 0
+
+
 FP8_INSTANCES = [(128, 64, 64), (128, 128, 64), (128, 128, 128)]
 
 
