@@ -49,7 +49,8 @@ def dense_causal_flops(seqlens, H, D):
 def measured_traffic(workload, dtype, dense):
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
     summary of this workload, if it was measured on the current kernel source
-    (else None)."""
+    (else None). The figure is replayed from that summary, not measured by
+    this run (rocprofv3 counters need a run of their own)."""
     import hashlib
 
     import re
@@ -169,7 +170,10 @@ def cpu_baseline(inp, w, lam, target_s=15.0):
     import oracle
     import synth
 
-    threads = int(os.environ.get("BSP_ORACLE_THREADS", "0")) or min(16, os.cpu_count() or 1)
+    nproc = os.cpu_count() or 1
+    avail = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else nproc
+    # the GPU machine gives one GPU's job a share of 16 host cores, whatever nproc shows
+    threads = int(os.environ.get("BSP_ORACLE_THREADS", "0")) or min(16, avail)
     L = inp.seqlens
     H, G = w.n_heads_q, w.n_heads_q // w.n_heads_kv
     head_order = [g + G * i for g in range(G) for i in range(H // G)]  # one head per KV head first
@@ -204,8 +208,134 @@ def cpu_baseline(inp, w, lam, target_s=15.0):
         "value": sum(L) / t_full, "unit": "tokens/s", "cores": threads, "kind": "oracle",
         "sample": f"{what}: {work.shape[0]} (head, tile) items, {pairs} of {total_pairs} visited (tile, block) "
                   f"pairs, lambda={lam}; {t_sample:.1f} s wall, scaled to the whole job by pairs",
-        "sample_seconds": round(t_sample, 2), "cpu": platform.processor() or platform.machine(),
+        "sample_seconds": round(t_sample, 2), "cpu_model": cpu_model(), "nproc": nproc, "affinity": avail,
+        "threads": threads,
+        "threads_note": ("BSP_ORACLE_THREADS" if os.environ.get("BSP_ORACLE_THREADS") else
+                         "min(16, CPUs this process may run on): the host-core share of one GPU on the GPU box"),
     }
+
+
+def cpu_model():
+    """Model name of the host CPU (from /proc/cpuinfo)."""
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def mfma_probe(steps=3):
+    """Measured matrix-core rate (TFLOP/s) of this GPU: the best of `steps`
+    runs of the probe kernels in libbsp_mfma_peak.so (chains of independent
+    bf16 / fp8 MFMAs on register operands, several waves per SIMD on every
+    compute unit), timed with HIP events on the launch stream."""
+    import ctypes
+
+    import torch
+
+    import block_sparse_long_bsp_amd.build as bld
+
+    lib = ctypes.CDLL(bld.PROBE_LIB)
+    lib.bsp_probe_mfma.restype = ctypes.c_int
+    lib.bsp_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.bsp_probe_mfma_flops.restype = ctypes.c_double
+    lib.bsp_probe_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks, iters = 8 * n_cu, 64
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    res = {}
+    for name, fp8 in (("bf16", 0), ("fp8", 1)):
+        best = 0.0
+        for i in range(steps + 1):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            rc = lib.bsp_probe_mfma(fp8, blocks, iters, ctypes.c_void_p(out.data_ptr()),
+                                    ctypes.c_void_p(stream.cuda_stream))
+            b.record(stream)
+            b.synchronize()
+            if rc != 0:
+                raise RuntimeError(f"probe launch failed ({rc})")
+            if i > 0:  # the first run warms up the clocks
+                best = max(best, lib.bsp_probe_mfma_flops(fp8, blocks, iters) / (a.elapsed_time(b) * 1e-3) / 1e12)
+        res[name] = best
+    return {"bf16_tflops": res["bf16"], "fp8_tflops": res["fp8"], "datasheet_bf16_tflops": PEAK_TFLOPS["bf16"],
+            "datasheet_fp8_tflops": PEAK_TFLOPS["fp8"], "compute_units": n_cu,
+            "what": "chains of independent v_mfma_f32_32x32x16_bf16 / v_mfma_scale_f32_32x32x64_f8f6f4 on register "
+                    "operands, 8 workgroups of 4 waves per compute unit; best of %d runs" % steps}
+
+
+def workload_row(bsp, name, dtype, steps, sparse_steps):
+    """Dense-mode and finite-lambda timings of another named workload (one
+    call of the C ABI over the whole workload per step), with its skip
+    fractions, executed TFLOP/s and roofline fraction."""
+    import torch
+
+    import synth
+
+    w = synth.WORKLOADS[name]
+    t0 = time.perf_counter()
+    inp = synth.make_workload(name, dtype)
+    gen_s = time.perf_counter() - t0
+
+    def up(a):
+        if dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+        if dtype == "fp8":
+            return torch.from_numpy(a).cuda().view(torch.float8_e4m3fn)
+        return torch.from_numpy(a).cuda()
+
+    q = up(inp.q)
+    k, v = (up(inp.k_pages), up(inp.v_pages)) if w.paged else (up(inp.k), up(inp.v))
+    table = torch.from_numpy(inp.block_table).cuda() if w.paged else None
+    cu = torch.from_numpy(inp.cu_seqlens).cuda()
+    scales = [None if x is None else torch.from_numpy(x).cuda() for x in (inp.q_scale, inp.k_scale, inp.v_scale)]
+    H, D = w.n_heads_q, w.head_dim
+    T = inp.total_tokens
+    o = torch.empty((T, H, D), dtype=torch.float32 if dtype == "f32" else torch.bfloat16, device="cuda")
+    lse = torch.empty((H, T), dtype=torch.float32, device="cuda")
+    sc = torch.empty((H,), dtype=torch.int64, device="cuda")
+    vc = torch.empty((H,), dtype=torch.int64, device="cuda")
+    visited = pair_counts(inp.seqlens, w.block_q, w.block_k) * H
+    unit = 2.0 * w.block_q * w.block_k * D
+    max_len = inp.max_seqlen
+    del inp
+
+    def call(lam):
+        return lambda: bsp.fwd(q, k, v, cu, max_len, block_table=table, block_q=w.block_q,
+                               block_k=w.block_k, lam=lam, q_scale=scales[0], k_scale=scales[1], v_scale=scales[2],
+                               out=o, lse=lse, want_bitmap=False, skip_count=sc, visited_count=vc)
+
+    rows = []
+    dense_ms = None
+    for lam in [math.inf] + [x for x in w.lambdas if not math.isinf(x)]:
+        ms = time_calls(call(lam), steps, 2)
+        kept = visited - int(sc.sum().item())
+        f = 1.0 - kept / visited
+        ex = unit * (visited + kept)
+        if dtype == "fp8":  # QK^T at the fp8 rate, PV at the bf16 rate
+            peak = ex / (unit * visited / PEAK_TFLOPS["fp8"] + unit * kept / PEAK_TFLOPS["bf16"])
+        else:
+            peak = PEAK_TFLOPS[dtype]
+        row = {"lambda": lam, "ms": ms, "tokens_per_s": T / (ms * 1e-3), "skip_fraction": f,
+               "executed_tflops": ex / (ms * 1e-3) / 1e12, "roofline_frac": ex / (ms * 1e-3) / 1e12 / peak}
+        if math.isinf(lam):
+            dense_ms = ms
+        else:
+            row["speedup_vs_dense"] = dense_ms / ms
+            row["flop_model_speedup"] = 1.0 / (1.0 - f / 2.0)
+        rows.append(row)
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
+    return {"workload": name, "dtype": dtype, "block_q": w.block_q, "block_k": w.block_k, "total_tokens": T,
+            "paged": w.paged, "generation_s": round(gen_s, 1), "rows": rows}
+
+
+EXTRA_WORKLOADS = (("llama8b_8k_bf16", "bf16"), ("varlen16_paged_bf16", "bf16"), ("llama8b_128k", "bf16"),
+                   ("llama8b_128k", "fp8"))
 
 
 def main():
@@ -221,6 +351,9 @@ def main():
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the decoding steps (single-sequence workloads); for kernel traces")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra-workloads", action="store_true",
+                    help="skip the rows of the other workloads (8K, varlen, 128K bf16 and fp8)")
+    ap.add_argument("--no-mfma-probe", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this size first (scales HBM byte counters)")
@@ -304,6 +437,11 @@ def main():
     exec_flops = unit_flops * (visited + kept)
     tokens_s = T_tok / (ms * 1e-3)
     exec_tflops = exec_flops / (ms * 1e-3) / 1e12
+    traffic = measured_traffic(w.name, dtype, True)
+    traffic_src = (None if traffic is None else
+                   "replayed from profiles/fwd_mfma_%s_%s_dense_hbm_bytes.json: rocprofv3 FETCH_SIZE and WRITE_SIZE "
+                   "passes on the same kernel source (SHA-256 matches), each scaled by a plain-copy calibration; "
+                   "not measured in this run" % (dtype, w.name.replace("_bf16", "").replace("_fp8", "")))
     # The fp8 kernel runs QK^T on the fp8 MFMA and PV on the bf16 MFMA: its
     # peak is the rate at which that mix of work can retire.
     if dtype == "fp8":
@@ -336,7 +474,8 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": exec_tflops / peak,
-            "traffic": measured_traffic(w.name, dtype, True),  # HBM bytes per launch (rocprofv3)
+            "traffic": traffic,  # HBM bytes per launch (rocprofv3), or None
+            "traffic_source": traffic_src,
             "per_launch": f"{visited} visited + {kept} kept (tile, block) pairs x 2*{w.block_q}*{w.block_k}*{D} "
                           f"FLOP = {exec_flops:.4g} FLOP",
         },
@@ -419,6 +558,18 @@ def main():
         result["chunked"] = rows
 
         result["decode"] = decode_rows(bsp, w, q, k, v, scales, dense_lam, finite, args.extra_steps)
+
+    if not args.no_mfma_probe:
+        result["roofline"]["measured_peak"] = mfma_probe()
+
+    if not args.no_extra_workloads and args.extra_steps > 0:
+        rows = []
+        for name, dt in EXTRA_WORKLOADS:
+            if (name, dt) == (w.name, dtype):
+                continue
+            print(f"# extra workload {name} ({dt})", file=sys.stderr, flush=True)
+            rows.append(workload_row(bsp, name, dt, args.extra_steps, args.extra_steps))
+        result["workloads"] = rows
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, w, dense_lam, target_s=args.cpu_seconds)

@@ -29,7 +29,7 @@ BSP_F32, BSP_BF16, BSP_FP8_E4M3 = 0, 1, 2
 
 EXPORTED = ("bsp_attn_fwd", "bsp_attn_fwd_ex", "bsp_attn_decode", "bsp_decode_workspace_bytes",
             "bsp_skip_bitmap_words", "bsp_skip_bitmap_words_kv", "bsp_status_string", "bsp_last_error_detail",
-            "bsp_version")
+            "bsp_version", "bsp_validate_host")
 
 # ablation switches of bsp_attn_fwd_ex (results unchanged, only the work done changes)
 FLAG_LOAD_SKIPPED_V = 1  # copy V also for blocks every query head of the workgroup skips
@@ -107,6 +107,9 @@ def load_library(path: str = LIB_PATH):
     lib.bsp_last_error_detail.argtypes = []
     lib.bsp_version.restype = ctypes.c_int
     lib.bsp_version.argtypes = []
+    lib.bsp_validate_host.restype = ctypes.c_int
+    lib.bsp_validate_host.argtypes = [P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                                      ctypes.c_int64, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64]
     _lib = lib
     return lib
 
@@ -127,6 +130,35 @@ def skip_bitmap_words_kv(n_heads_q: int, n_seqs: int, max_seqlen_q: int, max_seq
                          block_k: int) -> int:
     return int(load_library().bsp_skip_bitmap_words_kv(n_heads_q, n_seqs, max_seqlen_q, max_seqlen_k, block_q,
                                                        block_k))
+
+
+def validate_host(cu_seqlens_q, cu_seqlens_k=None, *, max_seqlen_q: int, max_seqlen_k: int = 0,
+                  total_q: int = -1, total_k: int = -1, block_table=None, page_size: int = 0,
+                  n_pages: int = 0) -> Tuple[int, str]:
+    """``bsp_validate_host`` on host arrays (numpy int32 or sequences):
+    returns (status, detail)."""
+    import numpy as np
+
+    lib = load_library()
+    cq = np.ascontiguousarray(cu_seqlens_q, dtype=np.int32)
+    ck = None if cu_seqlens_k is None else np.ascontiguousarray(cu_seqlens_k, dtype=np.int32)
+    bt = None if block_table is None else np.ascontiguousarray(block_table, dtype=np.int32)
+    if bt is not None and bt.ndim != 2:
+        raise ValueError("block_table must be [n_seqs, max_pages_per_seq]")
+    st = int(lib.bsp_validate_host(cq.ctypes.data, None if ck is None else ck.ctypes.data, len(cq) - 1,
+                                   int(max_seqlen_q), int(max_seqlen_k), int(total_q), int(total_k),
+                                   None if bt is None else bt.ctypes.data, 0 if bt is None else bt.shape[1],
+                                   int(page_size), int(n_pages)))
+    return st, last_error_detail() if st != BSP_OK else ""
+
+
+def _check_index_tensor(name: str, x: Optional[torch.Tensor], device, ndim: int) -> None:
+    """Descriptor arrays go to the kernels as raw int32 pointers: anything else
+    would be read as other values (e.g. int64 as pairs of int32)."""
+    if x is None:
+        return
+    if x.dtype != torch.int32 or not x.is_contiguous() or x.device != device or x.dim() != ndim:
+        raise ValueError(f"{name} must be a contiguous {ndim}-d torch.int32 tensor on {device}")
 
 
 def fwd_raw(q: Tensor, k: Tensor, v: Tensor, o: Tensor, lse_ptr: int, seqs: Seqs, block_table: Optional[BlockTable],
@@ -191,6 +223,8 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Ten
     if q.device.type != "cuda":
         raise ValueError("q must be a device tensor")
     T, Hq, D = q.shape
+    _check_index_tensor("cu_seqlens", cu_seqlens, q.device, 1)
+    _check_index_tensor("block_table", block_table, q.device, 2)
     paged = block_table is not None
     if paged:
         if k.dim() != 4:
@@ -271,6 +305,8 @@ def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_k: torc
     if q.device.type != "cuda":
         raise ValueError("q must be a device tensor")
     n_seqs, Hq, D = q.shape
+    _check_index_tensor("cu_seqlens_k", cu_seqlens_k, q.device, 1)
+    _check_index_tensor("block_table", block_table, q.device, 2)
     paged = block_table is not None
     if paged:
         if k.dim() != 4:

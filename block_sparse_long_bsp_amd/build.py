@@ -9,6 +9,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "bsp_attn.hip")
 LIB = os.path.join(PKG, "libbsp_attn.so")
+# matrix-core rate probe used by the benchmark's roofline report (not part of the attention ABI)
+PROBE_SRC = os.path.join(PKG, "csrc", "mfma_peak.hip")
+PROBE_LIB = os.path.join(PKG, "libbsp_mfma_peak.so")
 INCLUDE = os.path.join(ROOT, "include")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc" if os.path.exists("/opt/rocm/bin/hipcc") else "hipcc")
@@ -26,19 +29,25 @@ FLAGS = [
 ]
 
 
-def build(extra=(), verbose=False) -> str:
-    """Compile ``csrc/bsp_attn.hip`` to ``libbsp_attn.so`` (always recompiles)."""
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC] + FLAGS + list(extra) + [SRC, "-o", tmp]
+def _compile(src, lib, extra=(), verbose=False) -> str:
+    tmp = lib + ".tmp%d" % os.getpid()
+    cmd = [HIPCC] + FLAGS + list(extra) + [src, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if "packed-fp32-ops" not in ln]
     if res.returncode != 0:
         sys.stderr.write("\n".join(msgs) + "\n")
-        raise RuntimeError("hipcc failed for %s" % SRC)
+        raise RuntimeError("hipcc failed for %s" % src)
     if verbose and msgs:
         print("\n".join(msgs))
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(extra=(), verbose=False) -> str:
+    """Compile ``csrc/bsp_attn.hip`` to ``libbsp_attn.so`` and the matrix-core
+    probe ``csrc/mfma_peak.hip`` to ``libbsp_mfma_peak.so`` (always recompiles)."""
+    _compile(PROBE_SRC, PROBE_LIB, verbose=verbose)
+    return _compile(SRC, LIB, extra, verbose)
 
 
 if __name__ == "__main__":

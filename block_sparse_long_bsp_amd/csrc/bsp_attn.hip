@@ -34,7 +34,9 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <cmath>
 #include <mutex>
+#include <vector>
 #include <type_traits>
 
 #include "bsp_attn.h"
@@ -2033,6 +2035,122 @@ bsp_status_t check_device() {
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// ---- debug validation of device-side descriptors (BSP_DEBUG_VALIDATE)
+//
+// The sequence bounds and page ids live in device memory, so the normal path
+// cannot check them without a synchronisation. With BSP_DEBUG_VALIDATE set
+// (to anything but "" or "0") each call first copies them to the host on its
+// stream, waits, and checks them, together with the extent of the device
+// allocations that hold q, k, v and o; a bad descriptor returns
+// BSP_ERR_INVALID_ARG and nothing is launched.
+bool debug_validate_enabled() {
+    const char *e = getenv("BSP_DEBUG_VALIDATE");
+    return e != nullptr && e[0] != '\0' && strcmp(e, "0") != 0;
+}
+
+bsp_status_t check_bounds(const char *name, const int32_t *cu, int32_t n, int32_t max_len, int64_t total) {
+    if (cu[0] != 0) return fail(BSP_ERR_INVALID_ARG, "%s[0] = %d, must be 0", name, cu[0]);
+    for (int32_t s = 0; s < n; ++s) {
+        const int64_t len = (int64_t)cu[s + 1] - cu[s];
+        if (len < 0) return fail(BSP_ERR_INVALID_ARG, "%s decreases at sequence %d (%d -> %d)", name, s, cu[s], cu[s + 1]);
+        if (len > max_len)
+            return fail(BSP_ERR_INVALID_ARG, "sequence %d has %lld positions in %s, above the stated maximum %d", s,
+                        (long long)len, name, max_len);
+    }
+    if (total >= 0 && cu[n] != total)
+        return fail(BSP_ERR_INVALID_ARG, "%s[n_seqs] = %d, but the call states %lld tokens", name, cu[n], (long long)total);
+    return BSP_OK;
+}
+
+// Highest element offset + 1 that an access of `rows` token slots of a
+// [slots, heads, head_dim] tensor reaches (rows > 0).
+int64_t tensor_extent_bytes(const bsp_tensor_t *x, int64_t rows, int heads, int head_dim) {
+    const int64_t es = elem_size(x->dtype);
+    return ((rows - 1) * x->stride_token + (int64_t)(heads - 1) * x->stride_head + head_dim) * es;
+}
+
+// Bytes from x->data to the end of the device allocation holding it (-1: not a device allocation).
+int64_t bytes_to_allocation_end(const void *ptr) {
+    void *base = nullptr;
+    size_t size = 0;
+    if (hipMemGetAddressRange(&base, &size, (void *)ptr) != hipSuccess || base == nullptr) {
+        (void)hipGetLastError();
+        return -1;
+    }
+    return (int64_t)((const char *)base + size - (const char *)ptr);
+}
+
+bsp_status_t check_extent(const char *name, const bsp_tensor_t *x, int64_t rows, int heads, int head_dim) {
+    if (rows <= 0) return BSP_OK;
+    const int64_t avail = bytes_to_allocation_end(x->data);
+    if (avail < 0) return fail(BSP_ERR_INVALID_ARG, "%s: data is not inside a device allocation", name);
+    const int64_t need = tensor_extent_bytes(x, rows, heads, head_dim);
+    if (need > avail)
+        return fail(BSP_ERR_INVALID_ARG, "%s: %lld rows need %lld bytes, the allocation holds %lld from the data pointer",
+                    name, (long long)rows, (long long)need, (long long)avail);
+    return BSP_OK;
+}
+
+// Physical pages whose every row a [slots, heads, head_dim] cache tensor holds.
+int64_t pages_held(const bsp_tensor_t *x, int page_size, int heads, int head_dim) {
+    const int64_t avail = bytes_to_allocation_end(x->data);
+    if (avail < 0) return 0;
+    const int64_t es = elem_size(x->dtype);
+    const int64_t tail = ((int64_t)(heads - 1) * x->stride_head + head_dim - x->stride_token) * es;
+    const int64_t per_page = (int64_t)page_size * x->stride_token * es;
+    return avail - tail < 0 ? 0 : (avail - tail) / per_page;
+}
+
+bsp_status_t copy_to_host(void *dst, const void *src, int64_t bytes, hipStream_t hs, const char *name) {
+    if (bytes <= 0) return BSP_OK;
+    if (hipMemcpyAsync(dst, src, (size_t)bytes, hipMemcpyDeviceToHost, hs) != hipSuccess ||
+        hipStreamSynchronize(hs) != hipSuccess) {
+        const hipError_t e = hipGetLastError();
+        return fail(BSP_ERR_INVALID_ARG, "BSP_DEBUG_VALIDATE: cannot read %s from the device (%s)", name,
+                    hipGetErrorString(e));
+    }
+    return BSP_OK;
+}
+
+// Copies the device descriptors of a call to the host and checks them (see above).
+// q_rows: query rows (rows of q and o); cu_k NULL: keys = queries.
+bsp_status_t validate_call(const bsp_tensor_t *q, const bsp_tensor_t *k, const bsp_tensor_t *v, const bsp_tensor_t *o,
+                           const int32_t *cu_q, const int32_t *cu_k, int32_t n_seqs, int32_t max_q, int32_t max_k,
+                           int64_t q_rows, int64_t total_q, int64_t total_k, const bsp_block_table_t *bt,
+                           const float *lam_seq, int n_heads_q, int n_heads_kv, int head_dim, hipStream_t hs) {
+    std::vector<int32_t> hq(cu_q ? n_seqs + 1 : 0), hk(cu_k ? n_seqs + 1 : 0);
+    std::vector<int32_t> table(bt ? (size_t)n_seqs * bt->max_pages_per_seq : 0);
+    std::vector<float> lams(lam_seq ? n_seqs : 0);
+    bsp_status_t st;
+    if (cu_q && (st = copy_to_host(hq.data(), cu_q, 4 * (int64_t)hq.size(), hs, "cu_seqlens")) != BSP_OK) return st;
+    if (cu_k && (st = copy_to_host(hk.data(), cu_k, 4 * (int64_t)hk.size(), hs, "cu_seqlens_k")) != BSP_OK) return st;
+    if (bt && (st = copy_to_host(table.data(), bt->table, 4 * (int64_t)table.size(), hs, "the block table")) != BSP_OK)
+        return st;
+    if (lam_seq && (st = copy_to_host(lams.data(), lam_seq, 4 * (int64_t)lams.size(), hs, "lambda_per_seq")) != BSP_OK)
+        return st;
+    int64_t n_pages = 0;
+    if (bt) {
+        const int64_t pk = pages_held(k, bt->page_size, n_heads_kv, head_dim);
+        const int64_t pv = pages_held(v, bt->page_size, n_heads_kv, head_dim);
+        n_pages = pk < pv ? pk : pv;
+        if (n_pages <= 0) return fail(BSP_ERR_INVALID_ARG, "the paged k/v tensors hold no whole page");
+    }
+    st = bsp_validate_host(cu_q ? hq.data() : nullptr, cu_k ? hk.data() : nullptr, n_seqs, max_q, max_k, total_q,
+                           bt ? -1 : total_k, bt ? table.data() : nullptr, bt ? bt->max_pages_per_seq : 0,
+                           bt ? bt->page_size : 0, n_pages);
+    if (st != BSP_OK) return st;
+    for (int32_t s = 0; s < (int32_t)lams.size(); ++s)
+        if (std::isnan(lams[s]) || lams[s] < 0.f)
+            return fail(BSP_ERR_INVALID_ARG, "lambda_per_seq[%d] = %g: must be >= 0 or +inf", s, lams[s]);
+    if ((st = check_extent("q", q, q_rows, n_heads_q, head_dim)) != BSP_OK) return st;
+    if ((st = check_extent("o", o, q_rows, n_heads_q, head_dim)) != BSP_OK) return st;
+    if (!bt) {
+        if ((st = check_extent("k", k, total_k, n_heads_kv, head_dim)) != BSP_OK) return st;
+        if ((st = check_extent("v", v, total_k, n_heads_kv, head_dim)) != BSP_OK) return st;
+    }
+    return BSP_OK;
+}
+
 // ---- decoding step: instances, chunking and workspace layout
 typedef void (*dec_fn)(DecParams);
 struct DecKernels {
@@ -2084,7 +2202,7 @@ DecLayout dec_layout(int n_heads_q, int n_heads_kv, int n_seqs, int64_t total_k,
 
 extern "C" {
 
-int bsp_version(void) { return 100; }
+int bsp_version(void) { return 200; }
 
 const char *bsp_status_string(int status) {
     switch (status) {
@@ -2107,6 +2225,40 @@ int64_t bsp_skip_bitmap_words_kv(int n_heads_q, int n_seqs, int max_seqlen_q, in
     const int64_t J = cdiv(max_seqlen_k, block_k);
     const int64_t W = cdiv(J, 32);
     return (int64_t)n_heads_q * n_seqs * T * W;
+}
+
+bsp_status_t bsp_validate_host(const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, int32_t n_seqs,
+                               int32_t max_seqlen_q, int32_t max_seqlen_k, int64_t total_q, int64_t total_k,
+                               const int32_t *block_table, int32_t max_pages_per_seq, int32_t page_size,
+                               int64_t n_pages) {
+    g_detail[0] = '\0';
+    if (n_seqs < 0 || cu_seqlens_q == nullptr) return fail(BSP_ERR_INVALID_ARG, "no sequence descriptor");
+    bsp_status_t st;
+    if ((st = check_bounds("cu_seqlens", cu_seqlens_q, n_seqs, max_seqlen_q, total_q)) != BSP_OK) return st;
+    const int32_t *cu_k = cu_seqlens_k ? cu_seqlens_k : cu_seqlens_q;
+    if (cu_seqlens_k != nullptr) {
+        if ((st = check_bounds("cu_seqlens_k", cu_k, n_seqs, max_seqlen_k, total_k)) != BSP_OK) return st;
+        for (int32_t s = 0; s < n_seqs; ++s)
+            if (cu_k[s + 1] - cu_k[s] < cu_seqlens_q[s + 1] - cu_seqlens_q[s])
+                return fail(BSP_ERR_INVALID_ARG, "sequence %d has %d queries but only %d keys", s,
+                            cu_seqlens_q[s + 1] - cu_seqlens_q[s], cu_k[s + 1] - cu_k[s]);
+    }
+    if (block_table != nullptr) {
+        if (page_size <= 0 || max_pages_per_seq < 0) return fail(BSP_ERR_INVALID_ARG, "bad page geometry");
+        for (int32_t s = 0; s < n_seqs; ++s) {
+            const int64_t pages = cdiv((int64_t)cu_k[s + 1] - cu_k[s], page_size);
+            if (pages > max_pages_per_seq)
+                return fail(BSP_ERR_INVALID_ARG, "sequence %d needs %lld pages, the table row holds %d", s,
+                            (long long)pages, max_pages_per_seq);
+            for (int64_t pg = 0; pg < pages; ++pg) {
+                const int32_t id = block_table[(int64_t)s * max_pages_per_seq + pg];
+                if (id < 0 || (n_pages > 0 && id >= n_pages))
+                    return fail(BSP_ERR_INVALID_ARG, "block_table[%d][%lld] = %d is outside the %lld pages of the cache",
+                                s, (long long)pg, id, (long long)n_pages);
+            }
+        }
+    }
+    return BSP_OK;
 }
 
 int64_t bsp_skip_bitmap_words(int n_heads_q, int n_seqs, int max_seqlen, int block_q, int block_k) {
@@ -2230,6 +2382,19 @@ bsp_status_t bsp_attn_fwd_ex(const bsp_tensor_t *q, const bsp_tensor_t *k, const
     // ---------------- device
     if ((st = check_device()) != BSP_OK) return st;
     hipStream_t hs = (hipStream_t)stream;
+    if (debug_validate_enabled()) {
+        const int64_t total_k = chunked ? -1 : seqs->total_tokens;  // with cu_seqlens_k: cu_k[n] itself
+        st = validate_call(q, k, v, o, seqs->cu_seqlens, opts->cu_seqlens_k, seqs->n_seqs, seqs->max_seqlen, max_k,
+                           seqs->total_tokens, seqs->total_tokens, total_k, bt, opts->lambda_per_seq, n_heads_q,
+                           n_heads_kv, head_dim, hs);
+        if (st != BSP_OK) return st;
+        if (chunked && !paged) {  // the packed k/v rows the keys address
+            int32_t last = 0;
+            if ((st = copy_to_host(&last, opts->cu_seqlens_k + seqs->n_seqs, 4, hs, "cu_seqlens_k")) != BSP_OK) return st;
+            if ((st = check_extent("k", k, last, n_heads_kv, head_dim)) != BSP_OK) return st;
+            if ((st = check_extent("v", v, last, n_heads_kv, head_dim)) != BSP_OK) return st;
+        }
+    }
     unsigned long long *c0 = skip_out ? skip_out->skip_count : nullptr;
     unsigned long long *c1 = skip_out ? skip_out->visited_count : nullptr;
     unsigned long long *c2 = opts->skip_count_per_seq;
@@ -2378,6 +2543,15 @@ bsp_status_t bsp_attn_decode(const bsp_tensor_t *q, const bsp_tensor_t *k, const
 
     if ((st = check_device()) != BSP_OK) return st;
     hipStream_t hs = (hipStream_t)stream;
+    if (debug_validate_enabled()) {
+        // the keys as seqs_k states them; one query row per sequence (rows of q and o)
+        st = validate_call(q, k, v, o, seqs_k->cu_seqlens, nullptr, n_seqs, seqs_k->max_seqlen, seqs_k->max_seqlen, 0,
+                           seqs_k->total_tokens, seqs_k->total_tokens, bt, opts->lambda_per_seq, n_heads_q,
+                           n_heads_kv, head_dim, hs);
+        if (st != BSP_OK) return st;
+        if ((st = check_extent("q", q, n_seqs, n_heads_q, head_dim)) != BSP_OK) return st;
+        if ((st = check_extent("o", o, n_seqs, n_heads_q, head_dim)) != BSP_OK) return st;
+    }
     unsigned long long *c0 = skip_out ? skip_out->skip_count : nullptr;
     unsigned long long *c1 = skip_out ? skip_out->visited_count : nullptr;
     unsigned long long *c2 = opts->skip_count_per_seq;

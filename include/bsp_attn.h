@@ -42,7 +42,17 @@
  * checks happen on the host before any HIP call, so a rejected call has no
  * effect on the device. bsp_last_error_detail() describes the last non-OK
  * status of the calling thread. Bad *device* data (cu_seqlens not
- * non-decreasing, page ids out of range) is not checked and can fault.
+ * non-decreasing, page ids out of range) is not checked on the normal path
+ * and can fault. Debug mode: with the environment variable
+ * BSP_DEBUG_VALIDATE set (to anything but "" or "0") every call first copies
+ * cu_seqlens (and cu_seqlens_k, the block table, lambda_per_seq) to the
+ * host on its stream, waits for the copy, and checks them with
+ * bsp_validate_host() below, together with the extent of the device
+ * allocations holding q, k, v and o (every row the call addresses must lie
+ * inside the allocation; for a paged cache this bounds the page ids). A bad
+ * descriptor returns BSP_ERR_INVALID_ARG with a detail string and launches
+ * nothing. The mode synchronises the stream on every call: it is for
+ * debugging, not for timing.
  */
 #ifndef BSP_ATTN_H
 #define BSP_ATTN_H
@@ -256,6 +266,28 @@ bsp_status_t bsp_attn_decode(const bsp_tensor_t *q, const bsp_tensor_t *k, const
                              const bsp_block_table_t *block_table, int n_heads_q, int n_heads_kv, int head_dim,
                              int block_k, float lambda, bsp_skip_out_t *skip_mask_out, void *stream,
                              const bsp_decode_options_t *options, void *workspace, int64_t workspace_bytes);
+
+/*
+ * Host-side check of sequence and page descriptors (host arrays), as the
+ * BSP_DEBUG_VALIDATE mode applies it to the copies of a call's device
+ * descriptors (the guide's section 5, step 4: packed dynamic batches and a
+ * paged KV cache). Returns BSP_OK, or BSP_ERR_INVALID_ARG with a detail
+ * string for the first problem found:
+ *   cu_seqlens_q   int32[n_seqs+1]: cu[0] = 0, non-decreasing, every length
+ *                  <= max_seqlen_q, cu[n_seqs] == total_q (total_q < 0: not checked).
+ *   cu_seqlens_k   int32[n_seqs+1] or NULL (keys = queries): the same with
+ *                  max_seqlen_k and total_k, and every sequence's key count >=
+ *                  its query count (chunked prefill).
+ *   block_table    int32[n_seqs][max_pages_per_seq] or NULL: the
+ *                  ceil(keys / page_size) pages each sequence reads must fit
+ *                  its row and hold ids in [0, n_pages) (n_pages <= 0: only
+ *                  ids >= 0 are checked).
+ * Touches no device and needs no GPU.
+ */
+bsp_status_t bsp_validate_host(const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, int32_t n_seqs,
+                               int32_t max_seqlen_q, int32_t max_seqlen_k, int64_t total_q, int64_t total_k,
+                               const int32_t *block_table, int32_t max_pages_per_seq, int32_t page_size,
+                               int64_t n_pages);
 
 /* Static text for a status code. */
 const char *bsp_status_string(int status);

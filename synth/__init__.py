@@ -420,3 +420,43 @@ def work_items(seqlens: Sequence[int], n_heads_q: int, block_q: int,
             for t in tiles:
                 out.append((s, h, t))
     return np.asarray(out, dtype=np.int32).reshape(-1, 3)
+
+
+def build_integer_inputs(seqlens: Sequence[int], n_heads_q: int, n_heads_kv: int, head_dim: int, dtype: str,
+                         qk_range: int = 3, code: int = 0, paged: bool = False, page_size: int = 64,
+                         sink_tokens: int = 4, sink_dims: int = 32) -> Inputs:
+    """Inputs whose q and k are small integers, uniform in [-qk_range, qk_range]
+    (v ~ N(0, 1)), stored as fp32 or bf16 (both exact for these values).
+    Sink structure in integers: on the first ``sink_dims`` dims every query
+    is positive (uniform in [1, qk_range]) and the first ``sink_tokens`` keys
+    of each sequence hold +qk_range, so those keys score high for every
+    query and many later blocks fall far below the running maximum.
+
+    Every product q_i k_i is then an integer and every dot product is an
+    integer well below 2^24, so fp32 accumulation (the GPU) and fp64 (the
+    oracle) give the same exact scores. With head_dim 64 the score scale
+    1/8 is a power of two, so a gap of g raw units is exactly g/8 in
+    natural-log units: a threshold lambda = g/8 puts that gap exactly on it.
+    """
+    if dtype not in ("f32", "bf16"):
+        raise ValueError("integer inputs are built for f32 and bf16 storage")
+    seqlens = tuple(int(x) for x in seqlens)
+    cu = np.zeros(len(seqlens) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(seqlens)
+    T = int(cu[-1])
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([BASE_SEED, code, _P_HEAD, 0, 0, 77])))
+    q = rng.integers(-qk_range, qk_range + 1, size=(T, n_heads_q, head_dim)).astype(np.float32)
+    k = rng.integers(-qk_range, qk_range + 1, size=(T, n_heads_kv, head_dim)).astype(np.float32)
+    v = rng.standard_normal((T, n_heads_kv, head_dim)).astype(np.float32)
+    sd = min(sink_dims, head_dim)
+    q[:, :, :sd] = rng.integers(1, qk_range + 1, size=(T, n_heads_q, sd))
+    for s0, L in zip(cu[:-1], seqlens):
+        k[s0: s0 + min(sink_tokens, L), :, :sd] = qk_range
+    w = Workload(name="integer", seqlens=seqlens, n_heads_q=n_heads_q, n_heads_kv=n_heads_kv, head_dim=head_dim,
+                 dtypes=(dtype,), block_q=0, block_k=0, lambdas=(), rho=0.0, n_vert=0, paged=paged,
+                 page_size=page_size, code=code)
+    inp = Inputs(workload=w, dtype=dtype, seqlens=seqlens, cu_seqlens=cu, q=_round_store(q, dtype),
+                 k=_round_store(k, dtype), v=_round_store(v, dtype))
+    if paged:
+        page_tensors(inp, page_size, code)
+    return inp

@@ -134,7 +134,10 @@ class Report:
     n_items: int = 0
     n_pairs: int = 0
     n_skipped: int = 0
-    n_band_flips: int = 0
+    n_band_flips: int = 0    # decisions that differ from the oracle's (all inside the band, else a problem)
+    n_flips_tight: int = 0   # ... of which with |margin| <= 1e-3
+    n_flips_wide: int = 0    # ... of which with 1e-3 < |margin| <= the dtype's band
+    max_flip_margin: float = 0.0
     max_abs: float = 0.0
     mean_abs: float = 0.0
     lse_max: float = 0.0
@@ -146,8 +149,13 @@ class Report:
 
 def compare(inp: synth.Inputs, gpu: Dict, block_q: int, block_k: int, lam: float,
             work: Optional[np.ndarray] = None, n_threads: int = 0, check_counts: bool = True,
-            chunk: Optional[Chunk] = None, lam_seq: Optional[Sequence[float]] = None) -> Report:
-    """Steps 2-6 of the protocol for the given work items (default: all)."""
+            chunk: Optional[Chunk] = None, lam_seq: Optional[Sequence[float]] = None,
+            band: Optional[float] = None) -> Report:
+    """Steps 2-6 of the protocol for the given work items (default: all).
+
+    ``band`` overrides the dtype's decision band (0: the bitmaps must be
+    identical, for inputs whose scores every side computes exactly)."""
+    band = MARGIN_BAND[inp.dtype] if band is None else band
     Hq = inp.q.shape[1]
     n_seqs = len(inp.seqlens)
     J = max(1, (inp.max_seqlen + block_k - 1) // block_k)
@@ -184,13 +192,17 @@ def compare(inp: synth.Inputs, gpu: Dict, block_q: int, block_k: int, lam: float
         lam_item = np.array([lam_of(int(s_)) for s_ in ref.work[:, 0]])[:, None]
         with np.errstate(invalid="ignore"):
             margin = np.abs(ref.mingap - lam_item)
-        hard = diff & ~(margin <= MARGIN_BAND[inp.dtype])
+        hard = diff & ~(margin <= band)
         if hard.any():
             idx = np.argwhere(hard)[:5]
             rep.problems.append(f"{int(hard.sum())} skip decisions differ outside the margin band, e.g. "
                                 + ", ".join(f"item{tuple(ref.work[i])} block {j} gap {ref.mingap[i, j]:.6g}"
                                             for i, j in idx))
         rep.n_band_flips = int(diff.sum())
+        soft = diff & ~hard
+        rep.n_flips_tight = int((soft & (margin <= 1e-3)).sum())
+        rep.n_flips_wide = int((soft & (margin > 1e-3)).sum())
+        rep.max_flip_margin = float(margin[soft].max()) if soft.any() else 0.0
         forced = np.where(vis, gbits, 0).astype(np.uint8)
         ref = run_ref(work=ref.work, forced=forced)
     rep.n_skipped = int((ref.skip.astype(bool) & vis).sum())
@@ -246,14 +258,28 @@ def compare(inp: synth.Inputs, gpu: Dict, block_q: int, block_k: int, lam: float
 
 def check_case(inp: synth.Inputs, block_q: int, block_k: int, lams: Sequence[float], paged: bool = False,
                work: Optional[np.ndarray] = None, dev=None, chunk: Optional[Chunk] = None,
-               lam_seq: Optional[Sequence[float]] = None, flags: int = 0, decode: bool = False) -> List[Report]:
-    """Run the GPU for each lambda and compare; raise AssertionError on any problem."""
+               lam_seq: Optional[Sequence[float]] = None, flags: int = 0, decode: bool = False,
+               band: Optional[float] = None) -> List[Report]:
+    """Run the GPU for each lambda and compare; raise AssertionError on any problem.
+
+    Every report's flip counts are also added to ``FLIP_TALLY`` (per dtype)."""
     dev = dev or to_device(inp)
     reps = []
     for lam in lams:
         gpu = run_gpu(inp, dev, block_q, block_k, lam, paged=paged, chunk=chunk, lam_seq=lam_seq, flags=flags,
                       decode=decode)
-        rep = compare(inp, gpu, block_q, block_k, lam, work=work, chunk=chunk, lam_seq=lam_seq)
+        rep = compare(inp, gpu, block_q, block_k, lam, work=work, chunk=chunk, lam_seq=lam_seq, band=band)
         reps.append(rep)
-        assert rep.ok(), f"lambda={lam}: " + "; ".join(rep.problems)
+        t = FLIP_TALLY.setdefault(inp.dtype, dict(pairs=0, tight=0, wide=0, max_margin=0.0))
+        t["pairs"] += rep.n_pairs
+        t["tight"] += rep.n_flips_tight
+        t["wide"] += rep.n_flips_wide
+        t["max_margin"] = max(t["max_margin"], rep.max_flip_margin)
+        assert rep.ok(), (f"lambda={lam}: " + "; ".join(rep.problems)
+                          + f" [flips: {rep.n_flips_tight} with |margin| <= 1e-3, {rep.n_flips_wide} wider]")
     return reps
+
+
+# Decision flips (GPU vs oracle) seen by check_case in this process, per input dtype:
+# visited pairs compared, flips with |margin| <= 1e-3, flips with a wider margin.
+FLIP_TALLY: Dict[str, Dict[str, float]] = {}

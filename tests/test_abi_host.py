@@ -293,3 +293,43 @@ def test_decode_invalid_arguments_rejected_before_the_device(lib, case, expect):
     st = _call_dec(**case)
     assert st == expect, (st, bsp.last_error_detail())
     assert bsp.last_error_detail() != ""
+
+
+# ---- bsp_validate_host: the checks BSP_DEBUG_VALIDATE applies to copies of a call's device descriptors
+
+def test_validate_host_accepts_good_descriptors(lib):
+    cu = [0, 300, 300, 429]
+    assert bsp.validate_host(cu, max_seqlen_q=300, total_q=429) == (bsp.BSP_OK, "")
+    # chunked: keys >= queries per sequence
+    assert bsp.validate_host([0, 45, 45, 46], [0, 300, 300, 429], max_seqlen_q=45, max_seqlen_k=300, total_q=46,
+                             total_k=429)[0] == bsp.BSP_OK
+    table = [[3, 1, 0, 0, 0], [0, 0, 0, 0, 0], [2, 4, 0, 0, 0]]  # 64-token pages; unused entries are not read
+    assert bsp.validate_host(cu, max_seqlen_q=300, block_table=table, page_size=128, n_pages=5)[0] == bsp.BSP_OK
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(cu_seqlens_q=[1, 300, 429], max_seqlen_q=300), "must be 0"),
+    (dict(cu_seqlens_q=[0, 300, 200, 429], max_seqlen_q=300), "decreases at sequence 1"),
+    (dict(cu_seqlens_q=[0, 300, 429], max_seqlen_q=200), "above the stated maximum"),
+    (dict(cu_seqlens_q=[0, 300, 429], max_seqlen_q=300, total_q=500), "states 500 tokens"),
+    (dict(cu_seqlens_q=[0, 45, 100], cu_seqlens_k=[0, 300, 350], max_seqlen_q=55, max_seqlen_k=300),
+     "has 55 queries but only 50 keys"),
+    (dict(cu_seqlens_q=[0, 45], cu_seqlens_k=[0, 300], max_seqlen_q=45, max_seqlen_k=200), "cu_seqlens_k"),
+    (dict(cu_seqlens_q=[0, 300, 429], max_seqlen_q=300, block_table=[[0, 1], [2, 3]], page_size=128, n_pages=8),
+     "needs 3 pages"),
+    (dict(cu_seqlens_q=[0, 300, 429], max_seqlen_q=300, block_table=[[0, 1, 2], [3, -1, 0]], page_size=128,
+          n_pages=8), "block_table[1][1] = -1"),
+    (dict(cu_seqlens_q=[0, 300, 429], max_seqlen_q=300, block_table=[[0, 1, 2], [3, 8, 0]], page_size=128,
+          n_pages=8), "block_table[1][1] = 8"),
+])
+def test_validate_host_rejects_bad_descriptors(lib, kw, needle):
+    st, detail = bsp.validate_host(**kw)
+    assert st == bsp.BSP_ERR_INVALID_ARG
+    assert needle in detail, detail
+
+
+def test_validate_host_reads_only_pages_in_use(lib):
+    # entries past a sequence's ceil(len / page) pages are never read, whatever they hold
+    table = [[0, 1, 2, 99999], [3, 4, -7, -7]]
+    assert bsp.validate_host([0, 300, 429], max_seqlen_q=300, block_table=table, page_size=128,
+                             n_pages=5)[0] == bsp.BSP_OK

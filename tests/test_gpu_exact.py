@@ -1,0 +1,159 @@
+"""GPU tests on inputs whose scores every side computes exactly.
+
+* Strict comparison. With integer-valued q and k (bf16 or fp32 storage) and
+  head_dim 64 every score is an integer below 2^24, exact in the kernel's
+  fp32 accumulation and in the oracle's fp64, and the score scale 1/8 is a
+  power of two. A threshold lambda = g/8 then puts every (tile, block) pair
+  whose tile-wide minimum gap is g raw units exactly on the threshold. The
+  guide's section 6.1 calls a block negligible when the gap is strictly
+  greater than the threshold, so those pairs must be kept, and skipped at
+  lambda = g/8 - 1/16. No decision band applies: the GPU bitmap must equal
+  the oracle's bit for bit on every kernel variant (the two-head schedule at
+  128 x 128, its 64-key halves and 64-row half tiles, the one-head loop, the
+  fp32 kernel).
+
+* fp8 dot-product error. gfx950's fp8 MFMA does not round its sum of
+  products once: it drops low-order bits of the smaller products. With a
+  length-1 sequence the only key a query sees is key 0, so its LSE is the
+  scaled score read straight through the kernel's fp8 MFMA. Over crafted
+  vectors (one large product among many small ones, random codes, and
+  workload-like values) the error must stay within 3e-5 of
+  scale * s_q * s_k * sum_i |q_i k_i|: the bound the decision band for fp8
+  inputs rests on.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_sparse_long_bsp_amd as bsp
+
+    bsp.load_library()
+    yield
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+# (dtype, block_q, block_k, Hq, Hkv): bf16 with a group of 2 runs the two-head
+# schedule (128 x 128 as is; 64-key blocks as halves of 128-key blocks, with
+# 64-row half tiles at block_q 64); a group of 1 runs the one-head loop.
+TIE_CASES = [("bf16", 128, 128, 4, 2), ("bf16", 128, 64, 4, 2), ("bf16", 64, 64, 4, 2),
+             ("bf16", 128, 128, 2, 2), ("bf16", 64, 64, 2, 2),
+             ("f32", 64, 64, 2, 1), ("f32", 128, 64, 2, 1), ("f32", 128, 128, 2, 1)]
+
+
+@pytest.mark.parametrize("case", TIE_CASES, ids=lambda c: "%s_q%d_k%d_h%d_%d" % c)
+@pytest.mark.parametrize("paged", [False, True], ids=["packed", "paged"])
+def test_gap_equal_to_lambda_keeps_the_block(case, paged):
+    dtype, bq, bk, hq, hkv = case
+    inp = synth.build_integer_inputs((700, 300, 129), hq, hkv, 64, dtype, code=31, paged=paged, page_size=64)
+    J = (inp.max_seqlen + bk - 1) // bk
+    ref = oracle.run_inputs(inp, bq, bk, math.inf, j_max=J)
+    vis = ref.visited.astype(bool)
+    raw = ref.mingap * 8.0
+    fin = vis & np.isfinite(raw)
+    assert np.all(np.abs(raw[fin] - np.round(raw[fin])) < 1e-9), "raw gaps must be integers"
+    vals, counts = np.unique(np.round(raw[fin]).astype(np.int64), return_counts=True)
+    pos = vals > 0
+    vals, counts = vals[pos], counts[pos]
+    # the most frequent positive gap among the middle half of the sorted gaps
+    lo, hi = np.percentile(raw[fin & (raw > 0)], [25, 75])
+    mid = (vals >= lo) & (vals <= hi)
+    g = int(vals[mid][np.argmax(counts[mid])])
+    ties = fin & (np.round(raw) == g)
+    n_ties = int(ties.sum())
+    _log(f"tie case {case} paged={paged}: g={g} raw units, {n_ties} pairs exactly on lambda={g / 8}")
+    assert n_ties >= 1
+    dev = parity.to_device(inp)
+    for lam, tied_skipped in ((g / 8.0, False), (g / 8.0 - 1.0 / 16.0, True)):
+        gpu = parity.run_gpu(inp, dev, bq, bk, lam, paged=paged)
+        rep = parity.compare(inp, gpu, bq, bk, lam, band=0.0)
+        assert rep.ok(), f"lambda={lam}: " + "; ".join(rep.problems)
+        assert rep.n_band_flips == 0
+        gbits = np.stack([gpu["bits"][h, s, t, :J] for s, h, t in ref.work])
+        assert np.all(gbits[ties] == tied_skipped), "pairs with gap == g/8 must be kept at lambda = g/8 " \
+                                                    "and skipped just below it"
+        _log(f"  lambda={lam}: skipped {rep.n_skipped}/{rep.n_pairs}, bitmap identical to the oracle's")
+
+
+def _fp8_vectors(rng, n, D):
+    """Rows of fp8 e4m3 codes for q and k (n, D): three families."""
+    qs, ks = [], []
+    # 1) one large product among many small ones of mixed magnitude and sign
+    for _ in range(n // 3):
+        q = rng.uniform(-1, 1, D) * np.exp2(rng.integers(-9, -2, D))
+        k = rng.uniform(-1, 1, D) * np.exp2(rng.integers(-9, -2, D))
+        i = rng.integers(0, D)
+        q[i], k[i] = rng.uniform(200, 448), rng.uniform(200, 448) * rng.choice([-1, 1])
+        qs.append(q)
+        ks.append(k)
+    # 2) random codes over the whole finite range
+    for _ in range(n // 3):
+        qs.append(synth.fp8_e4m3_to_f32(rng.integers(0, 0x7E, D).astype(np.uint8)) * rng.choice([-1, 1], D))
+        ks.append(synth.fp8_e4m3_to_f32(rng.integers(0, 0x7E, D).astype(np.uint8)) * rng.choice([-1, 1], D))
+    # 3) workload-like: correlated normal vectors scaled into e4m3's range
+    while len(qs) < n:
+        x = rng.standard_normal(D)
+        qs.append((2 * x + rng.standard_normal(D)) * 60)
+        ks.append((2 * x + rng.standard_normal(D)) * 60)
+    return np.stack(qs), np.stack(ks)
+
+
+def test_fp8_mfma_score_error_bound():
+    import torch
+
+    import block_sparse_long_bsp_amd as bsp
+
+    D, n = 128, 768
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([synth.BASE_SEED, 91])))
+    qv, kv = _fp8_vectors(rng, n, D)
+    # two query heads (their own rows) share one KV head: the two-head schedule
+    q = np.stack([synth.fp8_e4m3_quantize(qv), synth.fp8_e4m3_quantize(qv[::-1])], axis=1)   # [n, 2, D]
+    k = synth.fp8_e4m3_quantize(kv)[:, None, :]                                                 # [n, 1, D]
+    v = synth.fp8_e4m3_quantize(rng.standard_normal((n, 1, D)))
+    qs = np.array([0.75, 1.25], dtype=np.float32)
+    ks = np.array([0.5], dtype=np.float32)
+    vs = np.array([1.0], dtype=np.float32)
+    cu = np.arange(n + 1, dtype=np.int32)  # n sequences of one token each
+    dq = torch.from_numpy(q).cuda().view(torch.float8_e4m3fn)
+    dk = torch.from_numpy(k).cuda().view(torch.float8_e4m3fn)
+    dv = torch.from_numpy(v).cuda().view(torch.float8_e4m3fn)
+    dcu = torch.from_numpy(cu).cuda()
+    sc = [torch.from_numpy(x).cuda() for x in (qs, ks, vs)]
+    worst = 0.0
+    for bq, bk, lam in ((128, 128, math.inf), (128, 128, 1.0), (64, 64, 1.0)):
+        o, lse, _, _, _ = bsp.fwd(dq, dk, dv, dcu, 1, block_q=bq, block_k=bk, lam=lam, q_scale=sc[0],
+                                  k_scale=sc[1], v_scale=sc[2])
+        torch.cuda.synchronize()
+        got = lse.cpu().numpy().astype(np.float64)  # [2, n]
+        qd = synth.fp8_e4m3_to_f32(q).astype(np.float64)
+        kd = synth.fp8_e4m3_to_f32(k).astype(np.float64)[:, 0, :]
+        for h in range(2):
+            prod = qd[:, h, :] * kd
+            scl = qs[h] * ks[0] / math.sqrt(D)
+            exact = scl * prod.sum(axis=1)
+            mag = scl * np.abs(prod).sum(axis=1)
+            err = np.abs(got[h] - exact)
+            # float rounding of the epilogue (score scale, log-sum-exp): a few ulps of the result
+            slack = 4 * np.finfo(np.float32).eps * (np.abs(exact) + mag) + 1e-30
+            ratio = (err - slack) / mag
+            worst = max(worst, float(ratio.max()))
+            assert np.all(err <= 3e-5 * mag + slack), \
+                f"head {h} ({bq}x{bk}, lambda={lam}): error {err.max():.3g} beyond 3e-5 of the scaled sum of |products|"
+    _log(f"fp8 MFMA score error: worst |error| / (scale * sum |q_i k_i|) = {worst:.3g} (bound 3e-5)")
