@@ -189,8 +189,11 @@ def _desc(x: torch.Tensor, scale: Optional[torch.Tensor] = None) -> Tensor:
         raise ValueError("head_dim must be contiguous")
     if x.dtype not in _DT:
         raise ValueError(f"unsupported dtype {x.dtype}")
-    return Tensor(x.data_ptr(), _DT[x.dtype], x.stride(0), x.stride(1),
-                  scale.data_ptr() if scale is not None else None)
+    # the stride of a dimension of size 1 is arbitrary (views from unsqueeze or
+    # [:, None] carry 0): never used for addressing, so pass a dense one
+    sh = x.stride(1) if x.shape[1] > 1 else x.shape[2]
+    st = x.stride(0) if x.shape[0] > 1 else x.shape[1] * sh
+    return Tensor(x.data_ptr(), _DT[x.dtype], st, sh, scale.data_ptr() if scale is not None else None)
 
 
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor, max_seqlen: int, *,

@@ -5,13 +5,13 @@ For one (inputs, block sizes, lambda) case:
   2. run the oracle on the same inputs for a set of work items (all, or a
      deterministic sample for large workloads);
   3. the skip bitmaps must be identical on every visited pair whose decision
-     margin |min gap - lambda| exceeds the band: 1e-3 for fp32 and bf16
-     inputs (scores are fp32 on the GPU and fp64 in the oracle, so pairs
-     inside that band may legitimately flip) and 1e-2 for fp8 inputs, whose
-     MFMA dot product is not rounded once at the end: measured on gfx950, it
-     drops low-order bits of the smaller products, an error up to ~3e-5 of
-     sum_i |q_i k_i|, i.e. up to ~3e-3 per score (~6.5e-3 per gap) on the
-     128K fp8 workload, where the scaled sum_i |q_i k_i| reaches ~107;
+     margin |min gap - lambda| exceeds the band of 1e-3 (scores are fp32 on
+     the GPU and fp64 in the oracle, so pairs inside that band may
+     legitimately flip). The same band holds for fp8 inputs: their MFMA dot
+     product does not round once (tests/test_gpu_exact.py pins its error
+     within 2^-11 of the scaled sum_i |q_i k_i|), but on the 128K fp8
+     workload every flip seen lies within 1e-3; the flip counts by margin
+     are reported (Report.n_flips_tight / n_flips_wide, FLIP_TALLY);
   4. where they differ inside the band, the oracle is re-run with the GPU's
      decisions forced, and outputs are compared against that run;
   5. O must satisfy the dtype's tolerance (bf16: max-abs <= 2e-2 and
@@ -32,7 +32,7 @@ import numpy as np
 import oracle
 import synth
 
-MARGIN_BAND = {"f32": 1e-3, "bf16": 1e-3, "fp8": 1e-2}
+MARGIN_BAND = {"f32": 1e-3, "bf16": 1e-3, "fp8": 1e-3}
 TOL = {
     "f32": dict(max_abs=1e-4, mean_abs=1e-4, lse=1e-4),
     "bf16": dict(max_abs=2e-2, mean_abs=2e-3, lse=1e-2),

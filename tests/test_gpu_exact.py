@@ -13,13 +13,15 @@
   fp32 kernel).
 
 * fp8 dot-product error. gfx950's fp8 MFMA does not round its sum of
-  products once: it drops low-order bits of the smaller products. With a
-  length-1 sequence the only key a query sees is key 0, so its LSE is the
-  scaled score read straight through the kernel's fp8 MFMA. Over crafted
-  vectors (one large product among many small ones, random codes, and
-  workload-like values) the error must stay within 3e-5 of
-  scale * s_q * s_k * sum_i |q_i k_i|: the bound the decision band for fp8
-  inputs rests on.
+  products once. With a length-1 sequence the only key a query sees is key 0,
+  so its LSE is the scaled score read straight through the kernel's fp8 MFMA.
+  Over crafted vectors (one large product among many small ones, random codes
+  over the whole e4m3 range, and workload-like values) the error stays within
+  2^-11 of scale * s_q * s_k * sum_i |q_i k_i|. Measured on the device: up to
+  about 3e-4 of that sum (and up to about 3.7e-4 of the largest single
+  product) when many large products of mixed magnitude add up, while a lone
+  dominant product keeps about 21 bits. The test pins that bound, which the
+  decision band for fp8 inputs has to respect.
 """
 
 import math
@@ -125,7 +127,7 @@ def test_fp8_mfma_score_error_bound():
     qv, kv = _fp8_vectors(rng, n, D)
     # two query heads (their own rows) share one KV head: the two-head schedule
     q = np.stack([synth.fp8_e4m3_quantize(qv), synth.fp8_e4m3_quantize(qv[::-1])], axis=1)   # [n, 2, D]
-    k = synth.fp8_e4m3_quantize(kv)[:, None, :]                                                 # [n, 1, D]
+    k = synth.fp8_e4m3_quantize(kv).reshape(n, 1, D)                                            # [n, 1, D]
     v = synth.fp8_e4m3_quantize(rng.standard_normal((n, 1, D)))
     qs = np.array([0.75, 1.25], dtype=np.float32)
     ks = np.array([0.5], dtype=np.float32)
@@ -136,7 +138,8 @@ def test_fp8_mfma_score_error_bound():
     dv = torch.from_numpy(v).cuda().view(torch.float8_e4m3fn)
     dcu = torch.from_numpy(cu).cuda()
     sc = [torch.from_numpy(x).cuda() for x in (qs, ks, vs)]
-    worst = 0.0
+    BOUND = 2.0 ** -11
+    worst = worst_max = 0.0
     for bq, bk, lam in ((128, 128, math.inf), (128, 128, 1.0), (64, 64, 1.0)):
         o, lse, _, _, _ = bsp.fwd(dq, dk, dv, dcu, 1, block_q=bq, block_k=bk, lam=lam, q_scale=sc[0],
                                   k_scale=sc[1], v_scale=sc[2])
@@ -154,6 +157,8 @@ def test_fp8_mfma_score_error_bound():
             slack = 4 * np.finfo(np.float32).eps * (np.abs(exact) + mag) + 1e-30
             ratio = (err - slack) / mag
             worst = max(worst, float(ratio.max()))
-            assert np.all(err <= 3e-5 * mag + slack), \
-                f"head {h} ({bq}x{bk}, lambda={lam}): error {err.max():.3g} beyond 3e-5 of the scaled sum of |products|"
-    _log(f"fp8 MFMA score error: worst |error| / (scale * sum |q_i k_i|) = {worst:.3g} (bound 3e-5)")
+            worst_max = max(worst_max, float(((err - slack) / (scl * np.abs(prod).max(axis=1))).max()))
+            assert np.all(err <= BOUND * mag + slack), \
+                f"head {h} ({bq}x{bk}, lambda={lam}): error {err.max():.3g} beyond 2^-11 of the scaled sum of |products|"
+    _log(f"fp8 MFMA score error: worst |error| / (scale * sum |q_i k_i|) = {worst:.3g} (bound {BOUND:.3g}); "
+         f"worst |error| / (scale * max |q_i k_i|) = {worst_max:.3g}")
