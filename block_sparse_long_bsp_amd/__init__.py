@@ -29,7 +29,10 @@ BSP_F32, BSP_BF16, BSP_FP8_E4M3 = 0, 1, 2
 
 EXPORTED = ("bsp_attn_fwd", "bsp_attn_fwd_ex", "bsp_attn_decode", "bsp_decode_workspace_bytes",
             "bsp_skip_bitmap_words", "bsp_skip_bitmap_words_kv", "bsp_status_string", "bsp_last_error_detail",
-            "bsp_version", "bsp_validate_host")
+            "bsp_version", "bsp_validate_host", "bsp_attn_decode_noalloc")
+
+# size of the static scratch array behind bsp_attn_decode_noalloc (BSP_DECODE_SCRATCH_BYTES)
+DECODE_SCRATCH_BYTES = 96 << 20
 
 # ablation switches of bsp_attn_fwd_ex (results unchanged, only the work done changes)
 FLAG_LOAD_SKIPPED_V = 1  # copy V also for blocks every query head of the workgroup skips
@@ -94,6 +97,8 @@ def load_library(path: str = LIB_PATH):
     lib.bsp_attn_decode.restype = ctypes.c_int
     lib.bsp_attn_decode.argtypes = [P, P, P, P, P, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                     ctypes.c_float, P, P, P, P, ctypes.c_int64]
+    lib.bsp_attn_decode_noalloc.restype = ctypes.c_int
+    lib.bsp_attn_decode_noalloc.argtypes = lib.bsp_attn_decode.argtypes[:-2]
     lib.bsp_decode_workspace_bytes.restype = ctypes.c_int64
     lib.bsp_decode_workspace_bytes.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
                                                ctypes.c_int, ctypes.c_int]
@@ -283,15 +288,16 @@ def decode_workspace_bytes(n_heads_q: int, n_heads_kv: int, n_seqs: int, total_k
                                                          head_dim, block_k))
 
 
-def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_k: torch.Tensor, max_seqlen_k: int, *,
-           total_k: Optional[int] = None, block_table: Optional[torch.Tensor] = None, block_k: int = 128,
-           lam: float = math.inf, q_scale: Optional[torch.Tensor] = None, k_scale: Optional[torch.Tensor] = None,
-           v_scale: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-           lse: Optional[torch.Tensor] = None, bitmap: Optional[torch.Tensor] = None,
-           skip_count: Optional[torch.Tensor] = None, visited_count: Optional[torch.Tensor] = None,
-           want_bitmap: bool = True, want_lse: bool = True, lam_per_seq: Optional[torch.Tensor] = None,
-           seq_skip_count: Optional[torch.Tensor] = None, seq_visited_count: Optional[torch.Tensor] = None,
-           flags: int = 0, workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, ...]:
+def _decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_k: torch.Tensor, max_seqlen_k: int, *,
+            total_k: Optional[int] = None, block_table: Optional[torch.Tensor] = None, block_k: int = 128,
+            lam: float = math.inf, q_scale: Optional[torch.Tensor] = None, k_scale: Optional[torch.Tensor] = None,
+            v_scale: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+            lse: Optional[torch.Tensor] = None, bitmap: Optional[torch.Tensor] = None,
+            skip_count: Optional[torch.Tensor] = None, visited_count: Optional[torch.Tensor] = None,
+            want_bitmap: bool = True, want_lse: bool = True, lam_per_seq: Optional[torch.Tensor] = None,
+            seq_skip_count: Optional[torch.Tensor] = None, seq_visited_count: Optional[torch.Tensor] = None,
+            flags: int = 0, workspace: Optional[torch.Tensor] = None,
+            noalloc: bool = False) -> Tuple[torch.Tensor, ...]:
     """One decoding step (``bsp_attn_decode``) on the current stream.
 
     q [n_seqs, Hq, D]: each sequence's new query row, which sees all of its
@@ -338,7 +344,7 @@ def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_k: torc
     need = decode_workspace_bytes(Hq, Hkv, n_seqs, int(total_k), int(max_seqlen_k), D, block_k)
     if need < 0:
         raise ValueError("invalid decode sizes")
-    if workspace is None:
+    if workspace is None and not noalloc:
         workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=q.device)
     for name, x, dt in (("cu_seqlens_k", cu_seqlens_k, torch.int32), ("lam_per_seq", lam_per_seq, torch.float32),
                         ("seq_skip_count", seq_skip_count, torch.int64),
@@ -354,16 +360,36 @@ def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_k: torc
                          seq_visited_count.data_ptr() if seq_visited_count is not None else None, int(flags))
     stream = torch.cuda.current_stream(q.device).cuda_stream
     lib = load_library()
-    st = int(lib.bsp_attn_decode(ctypes.byref(_desc(q, q_scale)), ctypes.byref(_desc(k3, k_scale)),
-                                 ctypes.byref(_desc(v3, v_scale)), ctypes.byref(_desc(out)),
-                                 ctypes.c_void_p(lse.data_ptr() if lse is not None else None), ctypes.byref(seqs),
-                                 ctypes.byref(bt) if bt is not None else None, Hq, Hkv, D, block_k,
-                                 ctypes.c_float(float(lam)), ctypes.byref(so), ctypes.c_void_p(stream or None),
-                                 ctypes.byref(opts), ctypes.c_void_p(workspace.data_ptr()),
-                                 ctypes.c_int64(workspace.numel() * workspace.element_size())))
+    args = (ctypes.byref(_desc(q, q_scale)), ctypes.byref(_desc(k3, k_scale)), ctypes.byref(_desc(v3, v_scale)),
+            ctypes.byref(_desc(out)), ctypes.c_void_p(lse.data_ptr() if lse is not None else None), ctypes.byref(seqs),
+            ctypes.byref(bt) if bt is not None else None, Hq, Hkv, D, block_k, ctypes.c_float(float(lam)),
+            ctypes.byref(so), ctypes.c_void_p(stream or None), ctypes.byref(opts))
+    if noalloc:
+        st = int(lib.bsp_attn_decode_noalloc(*args))
+    else:
+        st = int(lib.bsp_attn_decode(*args, ctypes.c_void_p(workspace.data_ptr()),
+                                     ctypes.c_int64(workspace.numel() * workspace.element_size())))
     if st != BSP_OK:
         raise BspError(st, last_error_detail())
     return out, lse, bitmap, skip_count, visited_count
+
+
+def decode(q, k, v, cu_seqlens_k, max_seqlen_k, **kw) -> Tuple[torch.Tensor, ...]:
+    """One decoding step through ``bsp_attn_decode`` (keyword arguments of
+    ``_decode``; ``workspace`` may be passed in to avoid an allocation)."""
+    return _decode(q, k, v, cu_seqlens_k, max_seqlen_k, **kw)
+
+
+def decode_noalloc(q, k, v, cu_seqlens_k, max_seqlen_k, **kw) -> Tuple[torch.Tensor, ...]:
+    """One decoding step through ``bsp_attn_decode_noalloc``: the library takes
+    the step's workspace from its static per-GPU scratch array instead of a
+    caller's buffer (at most ``DECODE_SCRATCH_BYTES``; calls that overlap in
+    time on one GPU race). The C call allocates nothing; pass every output
+    tensor (out, lse, bitmap, counts) to keep this function from allocating
+    them."""
+    if "workspace" in kw:
+        raise ValueError("decode_noalloc takes no workspace")
+    return _decode(q, k, v, cu_seqlens_k, max_seqlen_k, noalloc=True, **kw)
 
 
 def unpack_bitmap(bitmap: torch.Tensor, n_heads_q: int, n_seqs: int, max_seqlen: int, block_q: int,

@@ -2035,6 +2035,39 @@ bsp_status_t check_device() {
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// ---- static scratch of bsp_attn_decode_noalloc: the decoding step's workspace
+// (scores, block maxima, partial sums) for callers that cannot allocate. Every
+// GPU the library runs on holds its own copy until the process ends. Host code
+// never passes the array's name to a kernel (in host code it is a host-side
+// stand-in): it takes the device address that hipGetSymbolAddress returns,
+// once per device with that device current, and passes that.
+constexpr int64_t kScratchBytes = BSP_DECODE_SCRATCH_BYTES;
+__device__ __attribute__((aligned(256))) char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[64];  // per device: device address of `scratch`, or NULL until first use
+
+bsp_status_t scratch_address(void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return fail(BSP_ERR_DEVICE, "no current HIP device for the static scratch");
+    }
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || ptr == nullptr) {
+            (void)hipGetLastError();
+            return fail(BSP_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                        hipGetErrorString(e));
+        }
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return BSP_OK;
+}
+
 // ---- debug validation of device-side descriptors (BSP_DEBUG_VALIDATE)
 //
 // The sequence bounds and page ids live in device memory, so the normal path
@@ -2471,11 +2504,14 @@ int64_t bsp_decode_workspace_bytes(int n_heads_q, int n_heads_kv, int n_seqs, in
     return dec_layout(n_heads_q, n_heads_kv, n_seqs, total_k, max_seqlen_k, head_dim, block_k).bytes;
 }
 
-bsp_status_t bsp_attn_decode(const bsp_tensor_t *q, const bsp_tensor_t *k, const bsp_tensor_t *v, bsp_tensor_t *o,
-                             float *lse, const bsp_seqs_t *seqs_k, const bsp_block_table_t *bt, int n_heads_q,
-                             int n_heads_kv, int head_dim, int block_k, float lambda, bsp_skip_out_t *skip_out,
-                             void *stream, const bsp_decode_options_t *opts, void *workspace,
-                             int64_t workspace_bytes) {
+// bsp_attn_decode (caller's workspace) and bsp_attn_decode_noalloc (the static
+// scratch array of the current device) share everything but where the
+// workspace comes from.
+static bsp_status_t decode_call(const bsp_tensor_t *q, const bsp_tensor_t *k, const bsp_tensor_t *v, bsp_tensor_t *o,
+                                float *lse, const bsp_seqs_t *seqs_k, const bsp_block_table_t *bt, int n_heads_q,
+                                int n_heads_kv, int head_dim, int block_k, float lambda, bsp_skip_out_t *skip_out,
+                                void *stream, const bsp_decode_options_t *opts, void *workspace,
+                                int64_t workspace_bytes, bool use_scratch) {
     g_detail[0] = '\0';
     bsp_decode_options_t none;
     memset(&none, 0, sizeof(none));
@@ -2526,9 +2562,16 @@ bsp_status_t bsp_attn_decode(const bsp_tensor_t *q, const bsp_tensor_t *k, const
     const int n_seqs = seqs_k->n_seqs;
     const DecLayout L = dec_layout(n_heads_q, n_heads_kv, n_seqs, seqs_k->total_tokens, seqs_k->max_seqlen, head_dim,
                                    block_k);
-    if (workspace == nullptr || workspace_bytes < L.bytes || ((uintptr_t)workspace & 255u) != 0)
+    if (use_scratch) {
+        if (L.bytes > kScratchBytes)
+            return fail(BSP_ERR_INVALID_ARG,
+                        "the call needs %lld bytes of workspace, above the %lld-byte static scratch of "
+                        "bsp_attn_decode_noalloc (BSP_DECODE_SCRATCH_BYTES); pass a workspace to bsp_attn_decode",
+                        (long long)L.bytes, (long long)kScratchBytes);
+    } else if (workspace == nullptr || workspace_bytes < L.bytes || ((uintptr_t)workspace & 255u) != 0) {
         return fail(BSP_ERR_INVALID_ARG, "workspace needs %lld bytes, 256-byte aligned (got %lld)", (long long)L.bytes,
                     (long long)workspace_bytes);
+    }
     uint32_t *bitmap = skip_out ? skip_out->bitmap : nullptr;
     const int64_t words = bsp_skip_bitmap_words_kv(n_heads_q, n_seqs, 1, seqs_k->max_seqlen, 1, block_k);
     if (bitmap != nullptr) {
@@ -2542,6 +2585,7 @@ bsp_status_t bsp_attn_decode(const bsp_tensor_t *q, const bsp_tensor_t *k, const
         return fail(BSP_ERR_INVALID_ARG, "too many work items");
 
     if ((st = check_device()) != BSP_OK) return st;
+    if (use_scratch && (st = scratch_address(&workspace)) != BSP_OK) return st;
     hipStream_t hs = (hipStream_t)stream;
     if (debug_validate_enabled()) {
         // the keys as seqs_k states them; one query row per sequence (rows of q and o)
@@ -2620,6 +2664,24 @@ bsp_status_t bsp_attn_decode(const bsp_tensor_t *q, const bsp_tensor_t *k, const
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(BSP_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     return BSP_OK;
+}
+
+bsp_status_t bsp_attn_decode(const bsp_tensor_t *q, const bsp_tensor_t *k, const bsp_tensor_t *v, bsp_tensor_t *o,
+                             float *lse, const bsp_seqs_t *seqs_k, const bsp_block_table_t *bt, int n_heads_q,
+                             int n_heads_kv, int head_dim, int block_k, float lambda, bsp_skip_out_t *skip_out,
+                             void *stream, const bsp_decode_options_t *opts, void *workspace,
+                             int64_t workspace_bytes) {
+    return decode_call(q, k, v, o, lse, seqs_k, bt, n_heads_q, n_heads_kv, head_dim, block_k, lambda, skip_out, stream,
+                       opts, workspace, workspace_bytes, false);
+}
+
+bsp_status_t bsp_attn_decode_noalloc(const bsp_tensor_t *q, const bsp_tensor_t *k, const bsp_tensor_t *v,
+                                     bsp_tensor_t *o, float *lse, const bsp_seqs_t *seqs_k,
+                                     const bsp_block_table_t *bt, int n_heads_q, int n_heads_kv, int head_dim,
+                                     int block_k, float lambda, bsp_skip_out_t *skip_out, void *stream,
+                                     const bsp_decode_options_t *opts) {
+    return decode_call(q, k, v, o, lse, seqs_k, bt, n_heads_q, n_heads_kv, head_dim, block_k, lambda, skip_out, stream,
+                       opts, nullptr, 0, true);
 }
 
 }  // extern "C"

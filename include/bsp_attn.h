@@ -268,6 +268,31 @@ bsp_status_t bsp_attn_decode(const bsp_tensor_t *q, const bsp_tensor_t *k, const
                              const bsp_decode_options_t *options, void *workspace, int64_t workspace_bytes);
 
 /*
+ * bsp_attn_decode_noalloc -- bsp_attn_decode without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc). Arguments, results
+ * and errors are those of bsp_attn_decode; the workspace is instead a static
+ * device array of BSP_DECODE_SCRATCH_BYTES bytes inside the library, one per
+ * GPU, held from the first use on that GPU until the process ends. The call
+ * allocates and frees nothing (the array's device address is looked up once
+ * per device, on the first call there). Limit: calls whose
+ * bsp_decode_workspace_bytes(...) exceeds BSP_DECODE_SCRATCH_BYTES return
+ * BSP_ERR_INVALID_ARG before touching the device; 96 MiB holds e.g. 16
+ * contexts of 32K keys or 4 of 128K keys at 8 KV heads with 4 query heads
+ * each. All calls on one GPU share its array: calls that overlap in time on
+ * one GPU (other streams, other host threads) race and give wrong results;
+ * serialise them, or give each its own workspace through bsp_attn_decode.
+ * The array needs no initialisation (every call overwrites what it reads).
+ */
+#define BSP_DECODE_SCRATCH_BYTES (96LL << 20)
+
+bsp_status_t bsp_attn_decode_noalloc(const bsp_tensor_t *q, const bsp_tensor_t *k, const bsp_tensor_t *v,
+                                     bsp_tensor_t *o, float *lse, const bsp_seqs_t *seqs_k,
+                                     const bsp_block_table_t *block_table, int n_heads_q, int n_heads_kv,
+                                     int head_dim, int block_k, float lambda, bsp_skip_out_t *skip_mask_out,
+                                     void *stream, const bsp_decode_options_t *options);
+
+/*
  * Host-side check of sequence and page descriptors (host arrays), as the
  * BSP_DEBUG_VALIDATE mode applies it to the copies of a call's device
  * descriptors (the guide's section 5, step 4: packed dynamic batches and a

@@ -333,3 +333,23 @@ def test_validate_host_reads_only_pages_in_use(lib):
     table = [[0, 1, 2, 99999], [3, 4, -7, -7]]
     assert bsp.validate_host([0, 300, 429], max_seqlen_q=300, block_table=table, page_size=128,
                              n_pages=5)[0] == bsp.BSP_OK
+
+
+def test_decode_noalloc_rejects_calls_beyond_its_scratch_before_the_device(lib):
+    # 8 KV heads x 4 query heads x 4 bytes of scores per key: 10M keys need ~640 MB, above the static array
+    Hq, Hkv, D, bk = 32, 8, 128, 128
+    seqs = Seqs(FAKE, 2, 4096, 10_000_000)
+    need = bsp.decode_workspace_bytes(Hq, Hkv, seqs.n_seqs, seqs.total_tokens, seqs.max_seqlen, D, bk)
+    assert need > bsp.DECODE_SCRATCH_BYTES
+    q = Tensor(FAKE, bsp.BSP_BF16, Hq * D, D, None)
+    kv = Tensor(FAKE, bsp.BSP_BF16, Hkv * D, D, None)
+    o = Tensor(FAKE, bsp.BSP_BF16, Hq * D, D, None)
+    so = SkipOut(FAKE, bsp.skip_bitmap_words_kv(Hq, 2, 1, 4096, 1, bk), FAKE, FAKE)
+    st = int(lib.bsp_attn_decode_noalloc(ctypes.byref(q), ctypes.byref(kv), ctypes.byref(kv), ctypes.byref(o),
+                                         ctypes.c_void_p(FAKE), ctypes.byref(seqs), None, Hq, Hkv, D, bk,
+                                         ctypes.c_float(3.0), ctypes.byref(so), None, None))
+    assert st == bsp.BSP_ERR_INVALID_ARG
+    assert "static scratch" in bsp.last_error_detail()
+    # the header's constant and the binding's agree
+    text = open(HEADER).read()
+    assert "#define BSP_DECODE_SCRATCH_BYTES (96LL << 20)" in text and bsp.DECODE_SCRATCH_BYTES == 96 << 20
