@@ -20,7 +20,8 @@
 //     accumulator layout and V is stored transposed in LDS with the same
 //     permutation.
 //   * the tile-wide skip decision is a wave vote (__all) followed by an
-//     LDS AND across the waves; V is loaded only for kept blocks.
+//     LDS AND across the waves; V is loaded only for blocks some query head
+//     of the workgroup keeps.
 //   * work items are ordered heaviest tile first; when the KV head count is a
 //     multiple of 8 all query heads of one KV head run on one XCD (workgroup
 //     ids are dealt round-robin to the 8 XCDs), so its K/V stay in that
@@ -309,8 +310,11 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
     static_assert(!F8 || D == 128, "fp8 kernels are built for head_dim 128");
     __shared__ __attribute__((aligned(1024))) char sK[2][KBLKB];
     __shared__ __attribute__((aligned(1024))) char sV[NVB][VBLKB];
-    __shared__ __attribute__((aligned(1024))) char sV8[F8 ? KBLKB : 16];  // fp8 V staging
-    __shared__ int sVote[NW];
+    // fp8 V staging; the sparse two-head schedule can have the copies of two blocks in flight
+    constexpr int NV8 = (F8 && SPP) ? 2 : 1;
+    __shared__ __attribute__((aligned(1024))) char sV8[NV8][F8 ? KBLKB : 16];
+    __shared__ __attribute__((aligned(16))) int sVote[NW];
+    __shared__ int sHead;  // two-head sparse schedule: 1 if head 0 keeps the block it decided last
 
     int s, t, hp;
     decode_item(p, s, t, hp);  // hp: index of the head group served by this workgroup
@@ -421,8 +425,11 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
     static_assert((1 << kLog2Rpk) == KRPK, "rows per copy must be a power of two");
     const int crow0 = w * KRPK + lane / KCPR;
     const int lcK = 16 * ((lane % KCPR) ^ kswz(crow0));
-    auto copy_one = [&](const char *src, int64_t stb, int kb, char *dst, bool swz, int i) {
-        const int r = crow0 + i * CSTEP;
+    // dw: copy the share of wave w + dw instead of this wave's (the two-head sparse schedule lets
+    // the waves of one head copy a whole V block); |dw| * KRPK is a multiple of the swizzle period.
+    auto copy_one = [&](const char *src, int64_t stb, int kb, char *dst, bool swz, int i, int dw = 0) {
+        const int o = i * CSTEP + dw * KRPK;  // row offset of this copy from row crow0
+        const int r = crow0 + o;
         const int kk = min(kb + r, Lk - 1);
         const int lci = !swz ? 16 * (lane % KCPR) : kFixedChunk ? lcK : 16 * ((lane % KCPR) ^ kswz(r));
         if constexpr (PAGED) {
@@ -431,7 +438,7 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
                 // The instruction's KRPK rows (KRPK-aligned) lie in one page, also after
                 // clamping, so the page id is wave-uniform: a scalar load, which does
                 // not wait behind the copies in flight as a vector load would.
-                const int r0 = __builtin_amdgcn_readfirstlane(min(kb + w * KRPK + i * CSTEP, Lk - 1));
+                const int r0 = __builtin_amdgcn_readfirstlane(min(kb + w * KRPK + o, Lk - 1));
                 // read-only table through the constant address space: a uniform index
                 // becomes s_load_dword
                 const auto *tbl = (const __attribute__((address_space(4))) int32_t *)p.table;
@@ -439,20 +446,20 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
                     tbl[(int64_t)s * p.max_pages + min(r0 >> p.page_shift, p.max_pages - 1)]);
                 const char *pbase = src + ((int64_t)pg << p.page_shift) * stb;
                 lds_copy16_sb(pbase, (uint32_t)((kk & ((1 << p.page_shift) - 1)) * stb) + (uint32_t)lci,
-                              dst + (i * NW + w) * 1024);
+                              dst + (i * NW + w + dw) * 1024);
             } else {
-                lds_copy16(src + kv_row<PAGED>(p, s, kbase, kk, stb) + lci, dst + (i * NW + w) * 1024);
+                lds_copy16(src + kv_row<PAGED>(p, s, kbase, kk, stb) + lci, dst + (i * NW + w + dw) * 1024);
             }
         } else {
             // row kk - kb0 = min(r, lim) with lim = min(Lk - 1 - kb0, BK - 1), as
-            // min(crow0, lim - i*CSTEP) * stride + i*CSTEP * stride: one vector min and
-            // one add per copy (the per-lane crow0 * stride is loop-invariant); every
-            // term is below BK * stride < 2^31.
+            // min(crow0, lim - o) * stride + o * stride: one vector min and one add per
+            // copy (the per-lane crow0 * stride is loop-invariant); every term is below
+            // BK * stride < 2^31.
             const int kb0 = min(kb, Lk - 1);
             const int sb = (int)stb;
             const int lim = min(Lk - 1 - kb0, BK - 1);
-            const int rowb = min(crow0 * sb, (lim - i * CSTEP) * sb) + i * CSTEP * sb + lci;
-            lds_copy16_sb(src + (int64_t)(kbase + kb0) * stb, (uint32_t)rowb, dst + (i * NW + w) * 1024);
+            const int rowb = min(crow0 * sb, (lim - o) * sb) + o * sb + lci;
+            lds_copy16_sb(src + (int64_t)(kbase + kb0) * stb, (uint32_t)rowb, dst + (i * NW + w + dw) * 1024);
         }
     };
     auto copy_block = [&](const char *src, int64_t stb, int kb, char *dst, bool swz) {
@@ -461,13 +468,13 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
     };
     // fp8: widen this wave's own staged V bytes (its copies of the block, landed
     // once vmcnt says so) into the bf16 V buffer, in the bf16 row swizzle.
-    auto widen_v = [&](char *vdst) {
+    auto widen_v = [&](char *vdst, int stage = 0, int dw = 0) {
         if constexpr (F8) {
 #pragma unroll
             for (int i = 0; i < CI; ++i) {
-                const int r = crow0 + i * CSTEP;
+                const int r = crow0 + i * CSTEP + dw * KRPK;
                 const int c16 = lane % KCPR;
-                const u32x4 x = *(const u32x4 *)(sV8 + (i * NW + w) * 1024 + 16 * lane);
+                const u32x4 x = *(const u32x4 *)(sV8[stage] + (i * NW + w + dw) * 1024 + 16 * lane);
                 const u32x4 lo = {fp8x2_to_bf16x2<false>(x[0]), fp8x2_to_bf16x2<true>(x[0]),
                                   fp8x2_to_bf16x2<false>(x[1]), fp8x2_to_bf16x2<true>(x[1])};
                 const u32x4 hi = {fp8x2_to_bf16x2<false>(x[2]), fp8x2_to_bf16x2<true>(x[2]),
@@ -699,12 +706,16 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
         // M_{j-1}) ran in interval 2j - 1.
         auto issue_copy = [&](int j, int i) {  // copy i of this wave's share (K first, then V)
             if (i < CI) copy_one(kg, kstb, (j + 1) * BK, sK[(j + 1) & 1], true, i);
-            else if constexpr (F8) copy_one(vg, vstb, j * BK, sV8, false, i - CI);  // fp8 V: staged, widened later
+            else if constexpr (F8) copy_one(vg, vstb, j * BK, sV8[j & (NV8 - 1)], false, i - CI);  // fp8 V: staged, widened later
             else copy_one(vg, vstb, j * BK, sV[j & 1], true, i - CI);
+        };
+        auto copy_v = [&](int j) {  // this wave's share of V_j
+#pragma unroll
+            for (int i = CI; i < 2 * CI; ++i) issue_copy(j, i);
         };
         // fp8: once its copies of V_j have landed, each wave widens them into the bf16 buffer of block j
         auto land_v = [&](int j) {
-            if constexpr (F8) widen_v(sV[j & 1]);
+            if constexpr (F8) widen_v(sV[j & 1], j & (NV8 - 1));
         };
         // M phase: PV_{j-1} (probabilities pprev, V_{j-1} in LDS) and then QK_j
         // (K_j in LDS -> sacc). Only one wave of the SIMD issues matrix work in
@@ -828,12 +839,16 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
             }
             __builtin_amdgcn_s_setprio(0);
         };
-        auto qk_vote = [&](int j, auto do_copy) {  // QK_j, this interval's copies (if this wave issues them), vote
-            constexpr bool CP = decltype(do_copy)::value;
+        // QK_j with copy slots spread over its MFMAs (one every CSLOT), vote. With NCP = 2 CI slots,
+        // vmode (wave-uniform) picks the copies: bit 0 this wave's share of K_{j+1} (slots 0 .. CI-1),
+        // bit 1 its share of V_j (slots CI .. 2CI-1, or 0 .. CI-1 when K is not copied).
+        auto qk_vote = [&](int j, auto n_copies, int vmode = 3) {
+            constexpr int NCP = decltype(n_copies)::value;
+            constexpr bool CP = NCP > 0;
             constexpr int NQK = KS * MT;
             constexpr int PD = kPingPongDepth;
-            constexpr int CSLOT = NQK / (2 * CI);
-            static_assert(!CP || NQK % (2 * CI) == 0, "copies must spread evenly over the QK MFMAs");
+            constexpr int CSLOT = NQK / (CP ? NCP : 1);
+            static_assert(!CP || NQK % NCP == 0, "copies must spread evenly over the QK MFMAs");
             const char *kbuf = sK[j & 1];
             typedef typename std::conditional<F8, i32x8, bf16x8>::type KOp;
             KOp kop[NQK];
@@ -863,7 +878,13 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
                 if constexpr (CP) {
                     if (f % CSLOT == 0) {
                         SCHED_FENCE();
-                        issue_copy(j, f / CSLOT);
+                        const int i = f / CSLOT;
+                        if (i < CI) {
+                            if (vmode & 1) issue_copy(j, i);
+                            else if (vmode & 2) issue_copy(j, CI + i);
+                        } else if ((vmode & 3) == 3) {
+                            issue_copy(j, i);
+                        }
                     }
                 }
                 SCHED_FENCE();
@@ -903,21 +924,39 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
         // registers), row sum and bf16 probabilities. A skipped block zeroes the
         // probabilities instead, so that they are dead from a PV part to the next
         // vector phase on both paths (else they stay live through QK next to the
-        // scores). The interval's copies, when this wave issues them here, go
-        // first: interleaved with the exponentials they cost the instance its
-        // registers. Ablation (BSP_FLAG_EXP_SKIPPED): a skipped block's
-        // exponentials are taken on the kept path against +inf (its maximum is
-        // left out of the running max), so they come out zero and are dropped.
-        // Under key-half votes a block whose halves are decided apart runs the
-        // kept path, the skipped half's exponentials again taken against +inf.
-        auto v_sparse = [&](int j, auto do_copy, int cj) {
-            constexpr bool CP = decltype(do_copy)::value;
+        // scores). The copies this wave issues in its vector phase go right after
+        // the decision (after_vote(hk), hk = 1 if some wave of this head keeps
+        // block j): before the decision they delay its vote read, interleaved
+        // with the exponentials they cost the instance its registers.
+        // Ablation (BSP_FLAG_EXP_SKIPPED): a skipped block's exponentials are
+        // taken on the kept path against +inf (its maximum is left out of the
+        // running max), so they come out zero and are dropped. Under key-half
+        // votes a block whose halves are decided apart runs the kept path, the
+        // skipped half's exponentials again taken against +inf.
+        //
+        // head_keeps(x): 1 if some wave of head x keeps the block it last voted
+        // on (a vote: bit 0 first key half skipped; bits 1/2 second half
+        // skipped after a skipped / kept first half). One 16-byte LDS read,
+        // issued next to the wave's own vote reads.
+        auto head_keeps = [&](int x) -> int {
+            const u32x4 v = *(const u32x4 *)&sVote[x * WPH];
+            auto group_skips = [&](uint32_t vall) {
+                const bool ska = (vall & 1) != 0;
+                const bool skb = KH ? (((ska ? vall >> 1 : vall >> 2) & 1) != 0) : ska;
+                return ska && skb;
+            };
+            const bool sk = (KH && p.half_vote != 0) ? group_skips(v[0] & v[1]) && group_skips(v[2] & v[3])
+                                                     : group_skips(v[0] & v[1] & v[2] & v[3]);
+            return __builtin_amdgcn_readfirstlane(sk ? 0 : 1);
+        };
+        auto v_sparse = [&](int j, auto after_vote) {
             // the votes of this wave's head, or of its half-tile's two waves
             const int vmask = (KH && p.half_vote != 0) ? 3 << (wq & 2) : (1 << WPH) - 1;
             int vall = 7;
 #pragma unroll
             for (int y = 0; y < WPH; ++y)
                 if ((vmask >> y) & 1) vall &= sVote[hl * WPH + y];
+            const int hk = head_keeps(hl);
             vall = __builtin_amdgcn_readfirstlane(vall);
             bool ska, skb;  // decisions on the two key halves
             if constexpr (KH) {
@@ -931,10 +970,7 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
             }
             const bool sk = ska && skb;
             pend = !sk;
-            if constexpr (CP) {
-#pragma unroll
-                for (int i = 0; i < 2 * CI; ++i) issue_copy(cj, i);
-            }
+            after_vote(hk);
             if (!sk || (p.flags & BSP_FLAG_EXP_SKIPPED) != 0) {
                 float alpha, rs0 = 0.f, rs1 = 0.f;
                 bool resc;
@@ -974,41 +1010,104 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
         using F_ = std::false_type;
         const int n = nblk;
         if constexpr (SPP) {
+            // V-load skip. V_j is needed by head 0 in interval 2j + 2 and by
+            // head 1 in interval 2j + 3; it is copied once some head keeps
+            // block j, by the waves of that head alone (each wave its own share
+            // of the block and that of the other head's wave of the same index),
+            // right after they decide in their vector phase: head 0 in interval
+            // 2j + 1, when it keeps j; else head 1 in interval 2j + 2 (a late
+            // copy), when it keeps j. The copying waves wait for their copies
+            // before the barrier that ends the interval. When both heads skip j,
+            // V_j is never loaded. Head 0 publishes its decision in sHead during
+            // interval 2j + 1, and head 1 reads it in interval 2j + 2, so no
+            // wave reads another head's votes in its matrix phase. Block 0 is
+            // never skipped: V_0 goes with K_1 in interval 0.
+            using N0 = std::integral_constant<int, 0>;
+            using NK = std::integral_constant<int, CI>;        // this wave's share of K_{j+1}
+            using NKV = std::integral_constant<int, 2 * CI>;   // ... and of V_j
+            const bool v_all = (p.flags & BSP_FLAG_LOAD_SKIPPED_V) != 0;  // ablation: copy every V
+            const int dwo = hl == 0 ? WPH : -WPH;  // the other head's wave of the same index
+            auto copy_v_head = [&](int j) {
+#pragma unroll
+                for (int i = 0; i < CI; ++i) {
+                    issue_copy(j, CI + i);
+                    if constexpr (F8) copy_one(vg, vstb, j * BK, sV8[j & (NV8 - 1)], false, i, dwo);
+                    else copy_one(vg, vstb, j * BK, sV[j & 1], true, i, dwo);
+                }
+            };
+            auto land_v_head = [&](int j) {  // fp8: widen both shares
+                if constexpr (F8) {
+                    widen_v(sV[j & 1], j & (NV8 - 1));
+                    widen_v(sV[j & 1], j & (NV8 - 1), dwo);
+                }
+            };
             if (hl == 0) {
-                qk_vote(0, T_{});                         // interval 0
+                qk_vote(0, NKV{});                        // interval 0: K_1, V_0
                 __syncthreads();
-                v_sparse(0, F_{}, 0);                     // interval 1
+                v_sparse(0, [&](int) {                    // interval 1 (block 0 is kept)
+                    if (wq == 0 && lane == 0) sHead = 1;
+                });
                 wait_vmem_all();
                 land_v(0);
                 __syncthreads();
+                int h0k = 1;
                 for (int j = 1; j < n; ++j) {
-                    if (pend) pv_part(j);                 // interval 2j
-                    qk_vote(j, T_{});
+                    if (pend) pv_part(j);                 // interval 2j: PV_{j-1}, QK_j with K_{j+1}
+                    qk_vote(j, NK{});
                     __syncthreads();
-                    v_sparse(j, F_{}, 0);                 // interval 2j + 1
+                    bool cp = false;                      // interval 2j + 1: vector phase of block j
+                    v_sparse(j, [&](int hk) {
+                        h0k = hk;
+                        if (wq == 0 && lane == 0) sHead = hk;
+                        cp = hk != 0 || v_all;
+                        if (cp) copy_v_head(j);
+                    });
                     wait_vmem_all();
-                    land_v(j);
+                    if (cp) land_v_head(j);
                     __syncthreads();
                 }
-                if (pend) pv_part(n);                     // interval 2n
+                if (pend) pv_part(n);                     // interval 2n: PV_{n-1}
+                // head 1 copies V_{n-1} late when it keeps the block head 0 skipped (same test on both heads)
+                if (h0k == 0 && !v_all && head_keeps(1) != 0) __syncthreads();
             } else {
 #pragma unroll
                 for (int i = 0; i < 2 * CI; ++i) issue_copy(0, i);  // interval 0: K_1, V_0
                 __syncthreads();
-                qk_vote(0, F_{});                         // interval 1
+                qk_vote(0, N0{});                         // interval 1
                 wait_vmem_all();
                 land_v(0);
                 __syncthreads();
                 for (int j = 1; j < n; ++j) {
-                    v_sparse(j - 1, T_{}, j);             // interval 2j (copies of K_{j+1}, V_j)
+                    // interval 2j: vector phase of block j - 1; K_{j+1}, and V_{j-1} when this head keeps
+                    // the block head 0 skipped
+                    bool late = false;
+                    v_sparse(j - 1, [&](int hk) {
+                        const int h0k = __builtin_amdgcn_readfirstlane(sHead);
+#pragma unroll
+                        for (int i = 0; i < CI; ++i) issue_copy(j, i);
+                        late = hk != 0 && h0k == 0 && !v_all;
+                        if (late) copy_v_head(j - 1);
+                    });
+                    if (late) {
+                        wait_vmem_all();
+                        land_v_head(j - 1);
+                    }
                     __syncthreads();
-                    if (pend) pv_part(j);                 // interval 2j + 1
-                    qk_vote(j, F_{});
+                    if (pend) pv_part(j);                 // interval 2j + 1: PV_{j-1}, QK_j
+                    qk_vote(j, N0{});
                     wait_vmem_all();
-                    land_v(j);
                     __syncthreads();
                 }
-                v_sparse(n - 1, F_{}, 0);                 // interval 2n
+                bool late = false;                        // interval 2n: vector phase of block n-1
+                v_sparse(n - 1, [&](int hk) {
+                    late = hk != 0 && __builtin_amdgcn_readfirstlane(sHead) == 0 && !v_all;
+                    if (late) copy_v_head(n - 1);
+                });
+                if (late) {
+                    wait_vmem_all();
+                    land_v_head(n - 1);
+                    __syncthreads();
+                }
                 if (pend) pv_part(n);                     // interval 2n + 1
             }
         } else if (hl == 0) {
@@ -1060,7 +1159,7 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
         {
             const float mloc = qk_phase(0);
             __syncthreads();  // B1: every wave is done with QK_0
-            if constexpr (F8) copy_block(vg, vstb, 0, sV8, false);
+            if constexpr (F8) copy_block(vg, vstb, 0, sV8[0], false);
             else copy_block(vg, vstb, 0, sV[0], true);
             float alpha;
             bool resc;
@@ -1076,7 +1175,7 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
             wait_vmem_leave<CI>();
             widen_v(sV[0]);
             __syncthreads();  // B1
-            if constexpr (F8) copy_block(vg, vstb, j * BK, sV8, false);
+            if constexpr (F8) copy_block(vg, vstb, j * BK, sV8[0], false);
             else copy_block(vg, vstb, j * BK, sV[cur], true);
             float alpha;
             bool resc;
@@ -1120,7 +1219,7 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
             // ablation: copy V also for blocks every head skips
             any_keep = any_keep || (p.flags & BSP_FLAG_LOAD_SKIPPED_V) != 0;
             if (any_keep) {
-                if constexpr (F8) copy_block(vg, vstb, kb, sV8, false);
+                if constexpr (F8) copy_block(vg, vstb, kb, sV8[0], false);
                 else copy_block(vg, vstb, kb, sV[cur], true);
             }
             // Exponentials in place, then the pending PV, then row sum, rescale and
@@ -1229,7 +1328,8 @@ __global__ void __launch_bounds__(BQ * 2) fwd_f32(FwdParams p) {
     constexpr int STR = D + 1;
     __shared__ float sK[BK * STR];
     __shared__ float sV[BK * STR];
-    __shared__ int sVote[NW];
+    __shared__ __attribute__((aligned(16))) int sVote[NW];
+    __shared__ int sHead;  // two-head sparse schedule: 1 if head 0 keeps the block it decided last
 
     int s, t, h;
     decode_item(p, s, t, h);

@@ -172,11 +172,12 @@ int64_t bsp_skip_bitmap_words(int n_heads_q, int n_seqs, int max_seqlen, int blo
  *     settings, section 5, step 3): BSP_FLAG_LOAD_SKIPPED_V copies V also for
  *     blocks that every query head of the workgroup skips; BSP_FLAG_EXP_SKIPPED
  *     computes (and discards) the exponentials of skipped blocks. Results are
- *     unchanged; only the work done changes. Kernels whose schedule issues the
- *     V copy of a block before its decision (bf16, and fp8 with packed K/V,
- *     with an even GQA group, at any of the block sizes above) load every V
- *     block anyway, so BSP_FLAG_LOAD_SKIPPED_V changes nothing for them.
- *   Those calls run on 128-row tiles and 128-key blocks whatever block_q and
+ *     unchanged; only the work done changes. Without the first switch a V
+ *     block is read from memory only when some query head of the workgroup
+ *     keeps it (with an even GQA group the workgroup holds two query heads of
+ *     one KV head).
+ *   Sparse calls with an even GQA group (bf16, and fp8 with packed K/V)
+ *   run on 128-row tiles and 128-key blocks whatever block_q and
  *   block_k are. Each 64-row half of a tile and each 64-key half of a block is
  *   then decided on its own, in key order, so the decisions, the bitmap and
  *   the counts are those of the caller's blocks. When one 64-key half of a
