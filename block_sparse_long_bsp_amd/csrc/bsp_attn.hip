@@ -161,6 +161,26 @@ __device__ __forceinline__ float max_fold16(float m, const f32x16 &a) {
 }
 __device__ __forceinline__ float wave_max16(const f32x16 &a) { return max_fold16(-INFINITY, a); }
 
+// Combine lanes l and l ^ 32 on the vector ALU: v_permlane32_swap of x with
+// itself yields [x_lo, x_lo] and [x_hi, x_hi] (lanes 0-31 and 32-63), so
+// every lane sees both halves without a round trip through LDS (ds_bpermute).
+// The sum is x_lo + x_hi on every lane, equal to x + x[l ^ 32] in either order.
+__device__ __forceinline__ void lane_halves(float x, float &lo, float &hi) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    lo = __uint_as_float(r[0]);
+    hi = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float halves_max(float x) {
+    float a, b;
+    lane_halves(x, a, b);
+    return fmaxf(a, b);
+}
+__device__ __forceinline__ float halves_sum(float x) {
+    float a, b;
+    lane_halves(x, a, b);
+    return a + b;
+}
+
 // Keeps the scheduler from moving any instruction across this point: the
 // interleaving written in the source (matrix, vector and copy instructions of
 // independent work) is kept at that granularity.
@@ -608,7 +628,7 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
         float m = -INFINITY;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) m = max_fold16(m, sacc[mt]);
-        return fmaxf(m, __shfl_xor(m, 32));
+        return halves_max(m);
     };
 
     // Running max, lazy reference update; returns (in mc) the reference in
@@ -628,7 +648,7 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
     // O and l to the new reference (after the pending PV), l += row sum, and the
     // bf16 probabilities of this block for its PV product.
     auto finish_block = [&](float rs, float alpha, bool resc) {
-        rs += __shfl_xor(rs, 32);
+        rs = halves_sum(rs);
         if (resc) {
             l_run *= alpha;
 #pragma unroll
@@ -790,7 +810,7 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
             float m = -INFINITY;
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) m = max_fold16(m, sacc[mt]);
-            m = fmaxf(m, __shfl_xor(m, 32));
+            m = halves_max(m);
             float alpha;
             bool resc;
             const float mc = new_reference(m, alpha, resc);
@@ -904,8 +924,8 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
                     if (mt < MT / 2) ma = max_fold16(ma, sacc[mt]);
                     else mb = max_fold16(mb, sacc[mt]);
                 }
-                mloc_a = fmaxf(ma, __shfl_xor(ma, 32));
-                mloc_b = fmaxf(mb, __shfl_xor(mb, 32));
+                mloc_a = halves_max(ma);
+                mloc_b = halves_max(mb);
                 vote = (__all(passes(m_dec, mloc_a)) ? 1 : 0) | (__all(passes(m_dec, mloc_b)) ? 2 : 0) |
                        (__all(passes(fmaxf(m_dec, mloc_a), mloc_b)) ? 4 : 0);
             } else {
@@ -913,7 +933,7 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
                 float m = -INFINITY;
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) m = max_fold16(m, sacc[mt]);
-                mloc_a = fmaxf(m, __shfl_xor(m, 32));
+                mloc_a = halves_max(m);
                 mloc_b = -INFINITY;
                 vote = __all(passes(m_dec, mloc_a)) ? 1 : 0;
             }
@@ -987,7 +1007,7 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
                     }
                 }
                 float rs = rs0 + rs1;
-                rs += __shfl_xor(rs, 32);
+                rs = halves_sum(rs);
                 if (resc) {
                     l_run *= alpha;
 #pragma unroll
@@ -1242,7 +1262,7 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
                 for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                     for (int i = 0; i < 16; ++i) rs += sacc[mt][i];
-                rs += __shfl_xor(rs, 32);
+                rs = halves_sum(rs);
                 if (resc) {
                     l_run *= alpha;
 #pragma unroll
