@@ -8,17 +8,21 @@
 // maximum, and when every row's gap exceeds lambda it skips the
 // exponentials, the V-block load and the PV product.
 //
-// Kernel organisation (one workgroup = one query tile of one query head):
-//   * block_q/32 waves of 64 lanes; wave w owns 32 query rows.
+// Kernel organisation (one workgroup = one query tile of one or two query
+// heads that share a KV head):
+//   * block_q/32 waves of 64 lanes per head; wave w owns 32 query rows.
 //   * scores are computed transposed, S^T = K Q^T, with 32x32 MFMA tiles:
 //     keys are the M dimension (read from LDS), queries the N dimension
 //     (held in registers for the whole tile). In the 32x32 accumulator
 //     layout lane l holds query (l % 32) and 16 keys, so every per-row
-//     reduction is 16 values in-lane plus one exchange with lane l ^ 32.
-//   * O^T = V^T P^T reuses the score accumulators directly as the B operand
-//     (bf16 path): the contraction index is permuted to match the
-//     accumulator layout and V is stored transposed in LDS with the same
-//     permutation.
+//     reduction is 16 values in-lane plus one exchange with lane l ^ 32
+//     (v_permlane32_swap).
+//   * O^T = V^T P^T reuses the score accumulators directly as the B operand:
+//     the contraction index is permuted to match the accumulator layout, and
+//     the V^T operand comes from row-major V in LDS through transposing reads
+//     (ds_read_b64_tr_b16).
+//   * with two heads per workgroup the waves of the two heads share the SIMDs
+//     and alternate matrix and vector phases half a block apart (ping-pong).
 //   * the tile-wide skip decision is a wave vote (__all) followed by an
 //     LDS AND across the waves; V is loaded only for blocks some query head
 //     of the workgroup keeps.
@@ -836,13 +840,13 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
         // ---- sparse mode on the same schedule. The matrix phase is split into a
         // PV part, run only if this head kept block j - 1, with its own operand
         // prologue (so the branch around it leaves one register assignment), and
-        // a QK part that also carries the interval's copies and ends with this
+        // a QK part that also carries the interval's K copies and ends with this
         // wave's vote on block j (causal mask, row max, every valid row's gap to
         // the running max above lambda). The barrier after the matrix phase
         // publishes the votes; the vector phase reads the head's four votes,
         // records the decision, and for a kept block runs the reference update,
-        // exponentials and row sum. V_j is copied before any head has decided,
-        // so this schedule loads V for skipped blocks too.
+        // exponentials and row sum. V_j is copied only after a head has decided
+        // to keep block j (the V-load skip, below).
         float mloc_a = -INFINITY, mloc_b = -INFINITY;  // row maxima of the block's two key halves
         auto pv_part = [&](int j) {  // PV_{j-1}
             constexpr int PD = kPingPongDepth;
