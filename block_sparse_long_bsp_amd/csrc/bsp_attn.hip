@@ -2171,11 +2171,22 @@ __device__ __attribute__((aligned(256))) char scratch[kScratchBytes];
 std::mutex g_scratch_mu;
 void *g_scratch_ptr[64];  // per device: device address of `scratch`, or NULL until first use
 
-bsp_status_t scratch_address(void **out) {
+bsp_status_t scratch_address(hipStream_t stream, void **out) {
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
         (void)hipGetLastError();
         return fail(BSP_ERR_DEVICE, "no current HIP device for the static scratch");
+    }
+    // the kernels run on the stream's device and take the current device's copy of the array
+    if (stream != nullptr) {
+        hipDevice_t sdev = -1;
+        if (hipStreamGetDevice(stream, &sdev) != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(BSP_ERR_INVALID_ARG, "cannot query the device of the given stream");
+        }
+        if (sdev != dev)
+            return fail(BSP_ERR_INVALID_ARG, "the stream belongs to device %d but device %d is current", (int)sdev,
+                        dev);
     }
     std::lock_guard<std::mutex> lk(g_scratch_mu);
     if (g_scratch_ptr[dev] == nullptr) {
@@ -2709,8 +2720,8 @@ static bsp_status_t decode_call(const bsp_tensor_t *q, const bsp_tensor_t *k, co
         return fail(BSP_ERR_INVALID_ARG, "too many work items");
 
     if ((st = check_device()) != BSP_OK) return st;
-    if (use_scratch && (st = scratch_address(&workspace)) != BSP_OK) return st;
     hipStream_t hs = (hipStream_t)stream;
+    if (use_scratch && (st = scratch_address(hs, &workspace)) != BSP_OK) return st;
     if (debug_validate_enabled()) {
         // the keys as seqs_k states them; one query row per sequence (rows of q and o)
         st = validate_call(q, k, v, o, seqs_k->cu_seqlens, nullptr, n_seqs, seqs_k->max_seqlen, seqs_k->max_seqlen, 0,

@@ -284,6 +284,8 @@ bsp_status_t bsp_attn_decode(const bsp_tensor_t *q, const bsp_tensor_t *k, const
  * one GPU (other streams, other host threads) race and give wrong results;
  * serialise them, or give each its own workspace through bsp_attn_decode.
  * The array needs no initialisation (every call overwrites what it reads).
+ * The array used is that of the current device; a non-NULL stream of another
+ * device returns BSP_ERR_INVALID_ARG.
  */
 #define BSP_DECODE_SCRATCH_BYTES (96LL << 20)
 
