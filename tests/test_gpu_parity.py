@@ -105,6 +105,23 @@ def test_small_cases_fp8(inst, paged, gqa):
     assert reps[2].n_skipped > 0
 
 
+@pytest.mark.parametrize("inst", [(64, 64, 64), (128, 64, 64), (128, 128, 64), (128, 128, 128)],
+                         ids=lambda x: "d%d_q%d_k%d" % x)
+@pytest.mark.parametrize("cache", [(False, 64), (True, 16), (True, 64)], ids=["packed", "paged16", "paged64"])
+def test_small_cases_odd_group_bf16(inst, cache):
+    """bf16 with three query heads per KV head: one query head per workgroup (the lockstep loop, in both modes),
+    packed and paged; 16-token pages make the copies of 128-row tiles look their pages up per lane."""
+    D, bq, bk = inst
+    paged, page = cache
+    seqlens = (300, 0, 129, 1, 64)
+    inp = synth.build_inputs(seqlens, 3, 1, D, "bf16", rho=0.95, n_vert=2, code=216, paged=paged, page_size=page,
+                             sink_gain=6.0)
+    _log(f"small case bf16 odd group D={D} bq={bq} bk={bk} paged={paged} page={page}")
+    reps = parity.check_case(inp, bq, bk, [math.inf, 2.0, 0.0], paged=paged)
+    assert reps[0].n_skipped == 0
+    assert reps[2].n_skipped > 0
+
+
 def test_xcd_mapping_with_eight_kv_heads():
     # 8 KV heads switch on the XCD-partitioned work order
     inp = synth.build_inputs((517, 130), 16, 8, 128, "bf16", rho=0.97, n_vert=4, code=202)
