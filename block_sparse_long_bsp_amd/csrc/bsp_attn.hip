@@ -733,10 +733,6 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
             else if constexpr (F8) copy_one(vg, vstb, j * BK, sV8[j & (NV8 - 1)], false, i - CI);  // fp8 V: staged, widened later
             else copy_one(vg, vstb, j * BK, sV[j & 1], true, i - CI);
         };
-        auto copy_v = [&](int j) {  // this wave's share of V_j
-#pragma unroll
-            for (int i = CI; i < 2 * CI; ++i) issue_copy(j, i);
-        };
         // fp8: once its copies of V_j have landed, each wave widens them into the bf16 buffer of block j
         auto land_v = [&](int j) {
             if constexpr (F8) widen_v(sV[j & 1], j & (NV8 - 1));
