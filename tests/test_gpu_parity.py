@@ -155,6 +155,20 @@ def _sampled(name, heads, tile_stride, dtype=None):
     return reps
 
 
+def test_half_million_token_sequence_sampled():
+    """One sequence of 2^19 tokens, four times the longest workload: the 64-bit row offsets of Q, O, K and V, the
+    LSE and bitmap rows and the 4096-block tiles at sizes past those of the workloads. First, middle and last tile
+    of both query heads, dense and at lambda 3."""
+    L = 1 << 19
+    inp = synth.build_inputs((L,), 2, 1, 128, "bf16", rho=0.998, n_vert=64, code=217)
+    T = L // 128
+    work = synth.work_items((L,), 2, 128, heads=[0, 1], tile_stride=T, extra_tiles=(T // 2,))
+    _log(f"2^19-token sequence: {work.shape[0]} sampled work items")
+    reps = parity.check_case(inp, 128, 128, [math.inf, 3.0], work=work)
+    assert reps[1].n_skipped > 0
+    _log(f"  lambda=3: skipped {reps[1].n_skipped}/{reps[1].n_pairs}, max-abs {reps[1].max_abs:.3g}")
+
+
 def test_llama8b_8k_bf16_sampled():
     _sampled("llama8b_8k_bf16", heads=[0, 13, 31], tile_stride=7)
 
