@@ -637,10 +637,17 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
 
     // Running max, lazy reference update; returns (in mc) the reference in
     // base-2 units, and the rescale factor for O and l (resc: needed by a lane).
-    auto new_reference = [&](float mloc, float &alpha, bool &resc) -> float {
+    // On the blocks the causal mask cuts (those holding the tile's own keys) the
+    // reference follows every growth of the running max, so that a row whose
+    // weight sits on a nearby key gets probability exactly 1 there: a lagging
+    // reference would give it 2^d with d in (0, 8], which the bf16 rounding of P
+    // perturbs by up to 2^-9 of that key's whole contribution. At most one extra
+    // rescale per tile.
+    auto new_reference = [&](float mloc, int kb, float &alpha, bool &resc) -> float {
         const float m_new = fmaxf(m_dec, mloc);
         m_dec = m_new;
-        const bool need = (m_new - m_ref) * c > kRescaleLog2;  // also true while m_ref = -inf
+        const float lag = kb + BK - 1 > off + q0 ? 0.f : kRescaleLog2;
+        const bool need = (m_new - m_ref) * c > lag;  // also true while m_ref = -inf
         resc = __any(need);
         alpha = 1.f;
         if (need) {
@@ -813,7 +820,7 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
             m = halves_max(m);
             float alpha;
             bool resc;
-            const float mc = new_reference(m, alpha, resc);
+            const float mc = new_reference(m, kb, alpha, resc);
             float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
             for (int e = 0; e < NE; ++e) {
@@ -994,7 +1001,8 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
             if (!sk || (p.flags & BSP_FLAG_EXP_SKIPPED) != 0) {
                 float alpha, rs0 = 0.f, rs1 = 0.f;
                 bool resc;
-                const float mc = new_reference(fmaxf(ska ? -INFINITY : mloc_a, skb ? -INFINITY : mloc_b), alpha, resc);
+                const float mc = new_reference(fmaxf(ska ? -INFINITY : mloc_a, skb ? -INFINITY : mloc_b), j * BK, alpha,
+                                               resc);
                 // a skipped half's exponentials are taken against +inf: zero probabilities, zero sum
                 const float mca = ska ? INFINITY : mc, mcb = skb ? INFINITY : mc;
 #pragma unroll
@@ -1183,7 +1191,7 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
             else copy_block(vg, vstb, 0, sV[0], true);
             float alpha;
             bool resc;
-            const float mc = new_reference(mloc, alpha, resc);
+            const float mc = new_reference(mloc, 0, alpha, resc);
             finish_block(exp_sum(mc), alpha, resc);
             wait_vmem_leave<CI>();
             __syncthreads();  // B2: K_1 in LDS
@@ -1199,7 +1207,7 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
             else copy_block(vg, vstb, j * BK, sV[cur], true);
             float alpha;
             bool resc;
-            const float mc = new_reference(mloc, alpha, resc);
+            const float mc = new_reference(mloc, j * BK, alpha, resc);
             finish_block(fused_pv_exp(sV[F8 ? 0 : (cur ^ 1)], mc), alpha, resc);
             // B2: K_{j+1} is in LDS (loads complete in issue order; V_j, issued last, may still fly).
             wait_vmem_leave<CI>();
@@ -1249,7 +1257,7 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
             float alpha = 1.f;
             bool resc = false;
             if (!skip || (p.flags & BSP_FLAG_EXP_SKIPPED) != 0) {
-                const float mc = skip ? m_ref * c : new_reference(mloc, alpha, resc);
+                const float mc = skip ? m_ref * c : new_reference(mloc, kb, alpha, resc);
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
 #pragma unroll

@@ -122,6 +122,20 @@ def test_small_cases_odd_group_bf16(inst, cache):
     assert reps[2].n_skipped > 0
 
 
+@pytest.mark.parametrize("paged", [False, True], ids=["packed", "paged"])
+def test_two_hundred_ragged_sequences(paged):
+    """200 sequences of seeded random lengths in [0, 600] (zeros and single tokens among them) and 8 KV heads:
+    the work-item decoding, heaviest tile first, over many sequences and the XCD-partitioned order, on every
+    tile against the oracle."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([synth.BASE_SEED, 218])))
+    seqlens = [int(x) for x in rng.integers(0, 601, 200)]
+    seqlens[:4] = [0, 1, 600, 129]
+    inp = synth.build_inputs(seqlens, 16, 8, 128, "bf16", rho=0.95, n_vert=2, code=218, paged=paged, page_size=64)
+    _log(f"200 ragged sequences ({sum(seqlens)} tokens) paged={paged}")
+    reps = parity.check_case(inp, 64, 64, [math.inf, 2.0], paged=paged)
+    assert reps[1].n_skipped > 0
+
+
 def test_xcd_mapping_with_eight_kv_heads():
     # 8 KV heads switch on the XCD-partitioned work order
     inp = synth.build_inputs((517, 130), 16, 8, 128, "bf16", rho=0.97, n_vert=4, code=202)
