@@ -245,8 +245,9 @@ __device__ __forceinline__ void log_decision(const FwdParams &p, SkipLog &lg, in
 // cores and vector ALU overlap. The sparse kernel keeps step 3 unfused: the
 // skip branches and the fused order together do not fit in the registers.
 // The exponent reference max moves only when the running max has grown by
-// more than 2^8 (base-2 units), so the O/l rescale is rare; the running max
-// used by the skip decision is tracked exactly and separately.
+// more than 2^8 (base-2 units), so the O/l rescale is rare, except on the
+// blocks the causal mask cuts, where it follows the running max exactly; the
+// running max used by the skip decision is tracked exactly and separately.
 // ---------------------------------------------------------------------------
 constexpr float kRescaleLog2 = 8.0f;
 // LDS operand reads in flight ahead of the MFMA that uses them (dense ping-pong matrix phase).
