@@ -84,6 +84,48 @@ def time_calls(fn, steps, warmup):
     return start.elapsed_time(end) / steps  # ms per call
 
 
+def time_interleaved(fns, rounds, segment_ms=10.0, warmup_s=0.25):
+    """Mean call time of each callable in ``fns`` (a dict), taken in turns.
+
+    After a warm-up of at least ``warmup_s`` seconds of calls of all of them,
+    each round times one segment of back-to-back calls of every callable
+    (about ``segment_ms`` long; the order alternates between rounds), so that
+    clock and temperature drift reach all of them alike. Returns the median
+    over the rounds of each callable's per-call time (ms), and the calls per
+    segment."""
+    import statistics
+
+    import torch
+
+    stream = torch.cuda.current_stream()
+    t0 = time.perf_counter()
+    while True:
+        for fn in fns.values():
+            fn()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= warmup_s:
+            break
+
+    def segment(fn, n):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n):
+            fn()
+        b.record(stream)
+        b.synchronize()
+        return a.elapsed_time(b) / n
+
+    est = min(segment(fn, 1) for fn in fns.values())
+    calls = max(1, int(round(segment_ms / max(est, 1e-3))))
+    times = {key: [] for key in fns}
+    keys = list(fns)
+    for r in range(max(1, rounds)):
+        for key in (keys if r % 2 == 0 else keys[::-1]):
+            times[key].append(segment(fns[key], calls))
+    return {key: statistics.median(v) for key, v in times.items()}, calls
+
+
 def time_each(fn, steps, flush=None):
     """Median of per-call event timings; with ``flush`` (a callable writing a
     buffer larger than the last-level cache) run between calls, outside the
@@ -309,11 +351,18 @@ def workload_row(bsp, name, dtype, steps, sparse_steps):
                                block_k=w.block_k, lam=lam, q_scale=scales[0], k_scale=scales[1], v_scale=scales[2],
                                out=o, lse=lse, want_bitmap=False, skip_count=sc, visited_count=vc)
 
+    lams = [math.inf] + [x for x in w.lambdas if not math.isinf(x)]
+    skipped = {}
+    for lam in lams:  # one call each for the skip counts
+        call(lam)()
+        torch.cuda.synchronize()
+        skipped[lam] = int(sc.sum().item())
+    times, seg_calls = time_interleaved({lam: call(lam) for lam in lams}, rounds=sparse_steps)
     rows = []
     dense_ms = None
-    for lam in [math.inf] + [x for x in w.lambdas if not math.isinf(x)]:
-        ms = time_calls(call(lam), steps, 2)
-        kept = visited - int(sc.sum().item())
+    for lam in lams:
+        ms = times[lam]
+        kept = visited - skipped[lam]
         f = 1.0 - kept / visited
         ex = unit * (visited + kept)
         if dtype == "fp8":  # QK^T at the fp8 rate, PV at the bf16 rate
@@ -331,7 +380,9 @@ def workload_row(bsp, name, dtype, steps, sparse_steps):
     del q, k, v, o, lse
     torch.cuda.empty_cache()
     return {"workload": name, "dtype": dtype, "block_q": w.block_q, "block_k": w.block_k, "total_tokens": T,
-            "paged": w.paged, "generation_s": round(gen_s, 1), "rows": rows}
+            "paged": w.paged, "generation_s": round(gen_s, 1), "rows": rows,
+            "timing": f"every lambda (dense included) timed in turns: median over {max(1, sparse_steps)} rounds of "
+                      f"{seg_calls}-call segments, after a 0.25 s warm-up of all of them"}
 
 
 EXTRA_WORKLOADS = (("llama8b_8k_bf16", "bf16"), ("varlen16_paged_bf16", "bf16"), ("llama8b_128k", "bf16"),
@@ -345,9 +396,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama8b_32k_bf16")
     ap.add_argument("--dtype", default=None)
-    ap.add_argument("--sparse-steps", type=int, default=10)
+    ap.add_argument("--sparse-steps", type=int, default=10,
+                    help="rounds of the timing in turns of dense mode and the finite lambdas; 0 skips them")
     ap.add_argument("--extra-steps", type=int, default=10,
-                    help="calls per extra measurement (median/flushed timing, ablation, chunk, decode); 0 skips")
+                    help="calls per extra measurement (median/flushed timing, chunk, decode), and rounds of the timing in "
+                         "turns of the ablation switches and of the other workloads; 0 skips")
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the decoding steps (single-sequence workloads); for kernel traces")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -483,20 +536,34 @@ def main():
     }
 
     # ---- the workload's finite lambdas: skip fraction and speed-up over dense mode
+    # Dense mode and every finite lambda are timed in turns, so that the speed-ups
+    # compare calls made under the same clocks.
     sparse = []
-    for lam in lambdas:
-        if math.isinf(lam) or args.sparse_steps <= 0:
-            continue
-        ms_l = time_calls(call(lam), args.sparse_steps, 2)
-        skipped = int(sc.sum().item())
-        kept_l = visited - skipped
-        f = skipped / visited
-        sparse.append({
-            "lambda": lam, "ms": ms_l, "tokens_per_s": T_tok / (ms_l * 1e-3), "skip_fraction": f,
-            "executed_tflops": unit_flops * (visited + kept_l) / (ms_l * 1e-3) / 1e12,
-            "effective_tflops": dense_flops / (ms_l * 1e-3) / 1e12,
-            "speedup_vs_dense": ms / ms_l, "flop_model_speedup": 1.0 / (1.0 - f / 2.0),
-        })
+    finite_l = [x for x in lambdas if not math.isinf(x)]
+    if finite_l and args.sparse_steps > 0:
+        skipped_l = {}
+        for lam in finite_l:  # one call each for the skip counts
+            call(lam)()
+            torch.cuda.synchronize()
+            skipped_l[lam] = int(sc.sum().item())
+        fns = {dense_lam: call(dense_lam)}
+        fns.update({lam: call(lam) for lam in finite_l})
+        times, seg_calls = time_interleaved(fns, rounds=args.sparse_steps)
+        for lam in finite_l:
+            ms_l = times[lam]
+            kept_l = visited - skipped_l[lam]
+            f = skipped_l[lam] / visited
+            sparse.append({
+                "lambda": lam, "ms": ms_l, "tokens_per_s": T_tok / (ms_l * 1e-3), "skip_fraction": f,
+                "executed_tflops": unit_flops * (visited + kept_l) / (ms_l * 1e-3) / 1e12,
+                "effective_tflops": dense_flops / (ms_l * 1e-3) / 1e12,
+                "speedup_vs_dense": times[dense_lam] / ms_l, "flop_model_speedup": 1.0 / (1.0 - f / 2.0),
+            })
+        result["sparse_timing"] = {
+            "dense_ms": times[dense_lam],
+            "how": f"dense mode and each finite lambda timed in turns: median over {args.sparse_steps} rounds of "
+                   f"{seg_calls}-call segments after a 0.25 s warm-up; speed-ups are against this dense time",
+        }
     result["sparse"] = sparse
 
     # ---- per-call median, warm and with the last-level cache flushed between calls
@@ -521,15 +588,16 @@ def main():
                                    v_scale=scales[2], out=o, lse=lse, bitmap=bm, skip_count=sc,
                                    visited_count=vc, flags=fl)
 
-        ab = {}
-        for name, fl in (("skip_all", 0), ("load_skipped_v", bsp.FLAG_LOAD_SKIPPED_V),
-                         ("exp_skipped", bsp.FLAG_EXP_SKIPPED),
-                         ("load_v_and_exp_skipped", bsp.FLAG_LOAD_SKIPPED_V | bsp.FLAG_EXP_SKIPPED)):
-            ab[name] = time_calls(call_flags(fl), args.extra_steps, 2)
+        variants = (("skip_all", 0), ("load_skipped_v", bsp.FLAG_LOAD_SKIPPED_V),
+                    ("exp_skipped", bsp.FLAG_EXP_SKIPPED),
+                    ("load_v_and_exp_skipped", bsp.FLAG_LOAD_SKIPPED_V | bsp.FLAG_EXP_SKIPPED))
+        ab, seg_calls = time_interleaved({name: call_flags(fl) for name, fl in variants}, rounds=args.extra_steps)
         ab["skip_fraction"] = int(sc.sum().item()) / visited
         result["ablation"] = {"lambda": lam_a, "ms": ab, "dense_ms": ms,
                               "note": "flags keep the decisions and outputs; they only add back the V load "
-                                      "and/or the exps of skipped blocks"}
+                                      "and/or the exps of skipped blocks",
+                              "timing": f"the four variants timed in turns: median over {args.extra_steps} rounds "
+                                        f"of {seg_calls}-call segments after a 0.25 s warm-up"}
 
     # ---- chunked prefill against a cached prefix and one decoding step (single-sequence workloads)
     if args.extra_steps > 0 and len(inp.seqlens) == 1 and not w.paged and inp.seqlens[0] >= 16384:
