@@ -396,6 +396,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama8b_32k_bf16")
     ap.add_argument("--dtype", default=None)
+    ap.add_argument("--lambdas", default=None,
+                    help="comma-separated finite lambdas to time instead of the workload's own (e.g. 8)")
     ap.add_argument("--sparse-steps", type=int, default=10,
                     help="rounds of the timing in turns of dense mode and the finite lambdas; 0 skips them")
     ap.add_argument("--extra-steps", type=int, default=10,
@@ -470,7 +472,7 @@ def main():
                                block_k=w.block_k, lam=lam, q_scale=scales[0], k_scale=scales[1],
                                v_scale=scales[2], out=o, lse=lse, bitmap=bm, skip_count=sc, visited_count=vc)
 
-    lambdas = list(w.lambdas)
+    lambdas = list(w.lambdas) if args.lambdas is None else [float(x) for x in args.lambdas.split(",")]
     dense_lam = math.inf
     visited = pair_counts(inp.seqlens, w.block_q, w.block_k) * H
     unit_flops = 2.0 * w.block_q * w.block_k * D
