@@ -310,10 +310,11 @@ def mfma_probe(steps=3):
                     "operands, 8 workgroups of 4 waves per compute unit; best of %d runs" % steps}
 
 
-def workload_row(bsp, name, dtype, steps, sparse_steps):
+def workload_row(bsp, name, dtype, rounds):
     """Dense-mode and finite-lambda timings of another named workload (one
-    call of the C ABI over the whole workload per step), with its skip
-    fractions, executed TFLOP/s and roofline fraction."""
+    call of the C ABI over the whole workload per step, the lambdas timed in
+    turns over ``rounds`` rounds), with its skip fractions, executed TFLOP/s
+    and roofline fraction."""
     import torch
 
     import synth
@@ -357,7 +358,7 @@ def workload_row(bsp, name, dtype, steps, sparse_steps):
         call(lam)()
         torch.cuda.synchronize()
         skipped[lam] = int(sc.sum().item())
-    times, seg_calls = time_interleaved({lam: call(lam) for lam in lams}, rounds=sparse_steps)
+    times, seg_calls = time_interleaved({lam: call(lam) for lam in lams}, rounds=rounds)
     rows = []
     dense_ms = None
     for lam in lams:
@@ -381,7 +382,7 @@ def workload_row(bsp, name, dtype, steps, sparse_steps):
     torch.cuda.empty_cache()
     return {"workload": name, "dtype": dtype, "block_q": w.block_q, "block_k": w.block_k, "total_tokens": T,
             "paged": w.paged, "generation_s": round(gen_s, 1), "rows": rows,
-            "timing": f"every lambda (dense included) timed in turns: median over {max(1, sparse_steps)} rounds of "
+            "timing": f"every lambda (dense included) timed in turns: median over {max(1, rounds)} rounds of "
                       f"{seg_calls}-call segments, after a 0.25 s warm-up of all of them"}
 
 
@@ -638,7 +639,7 @@ def main():
             if (name, dt) == (w.name, dtype):
                 continue
             print(f"# extra workload {name} ({dt})", file=sys.stderr, flush=True)
-            rows.append(workload_row(bsp, name, dt, args.extra_steps, args.extra_steps))
+            rows.append(workload_row(bsp, name, dt, args.extra_steps))
         result["workloads"] = rows
 
     if not args.no_cpu_baseline:
