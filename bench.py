@@ -214,7 +214,7 @@ def cpu_baseline(inp, w, lam, target_s=15.0):
 
     nproc = os.cpu_count() or 1
     avail = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else nproc
-    # the GPU machine gives one GPU's job a share of 16 host cores, whatever nproc shows
+    # on a shared multi-GPU host one GPU's job gets a share of 16 host cores, whatever nproc shows
     threads = int(os.environ.get("BSP_ORACLE_THREADS", "0")) or min(16, avail)
     L = inp.seqlens
     H, G = w.n_heads_q, w.n_heads_q // w.n_heads_kv
@@ -253,7 +253,7 @@ def cpu_baseline(inp, w, lam, target_s=15.0):
         "sample_seconds": round(t_sample, 2), "cpu_model": cpu_model(), "nproc": nproc, "affinity": avail,
         "threads": threads,
         "threads_note": ("BSP_ORACLE_THREADS" if os.environ.get("BSP_ORACLE_THREADS") else
-                         "min(16, CPUs this process may run on): the host-core share of one GPU on the GPU box"),
+                         "min(16, CPUs this process may run on): the host-core share of one GPU on a shared host"),
     }
 
 
