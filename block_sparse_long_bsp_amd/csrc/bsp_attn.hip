@@ -1543,7 +1543,8 @@ __global__ void __launch_bounds__(BQ * 2) fwd_f32(FwdParams p) {
 // the KV group keeps, the scores written and read once. All vector ALU: four
 // query heads per KV head are too few rows for the matrix cores.
 // ---------------------------------------------------------------------------
-constexpr int kDecRows = 8;    // K/V row loads per wave in flight in the decode kernels
+constexpr int kDecRows = 8;    // V row loads per wave in flight in the decode PV kernel
+constexpr int kDecRowsS = 4;   // K row loads per batch in the decode score kernel (two batches in flight)
 constexpr int kDecMaxC = 256;  // key blocks per decode chunk, at most
 
 struct DecParams {
@@ -1722,56 +1723,86 @@ __global__ void __launch_bounds__(256) dec_scores(DecParams p) {
     const char *kg = (const char *)p.k + (int64_t)g * p.k_sh * ES;
     const int64_t kst = p.k_st * ES;
     float *Sg = p.S + ((int64_t)g * p.total_k + kbase) * GP;
-    // the chunk's blocks go round-robin to the 4 waves; a wave reduces its block alone
-    for (int j = j0 + w; j < j1; j += 4) {
-        const int kb = j * p.BK;
-        const int rows = min(p.BK, Lk - kb);
-        float bmax[GP];
+    // The chunk's blocks go round-robin to the 4 waves; a wave reduces its block
+    // alone. A wave's blocks are taken as one sequence of batches of kDecRowsS row
+    // loads (rows past a block re-read its last row), software-pipelined: the
+    // loads of the next batch are issued before the current one is computed.
+    constexpr int R = kDecRowsS;
+    constexpr int RB = RPW * R;  // rows per batch
+    auto block_rows = [&](int j) { return min(p.BK, Lk - j * p.BK); };
+    auto issue = [&](u32x4 (&xs)[R], int j, int r0) {
+        const int kb = j * p.BK, rows = block_rows(j);
 #pragma unroll
-        for (int h = 0; h < GP; ++h) bmax[h] = -INFINITY;
-        // kDecRows row loads in flight (rows past the block re-read its last row)
-        for (int r0 = 0; r0 < rows; r0 += RPW * kDecRows) {
-            u32x4 xs[kDecRows];
+        for (int u = 0; u < R; ++u) {
+            const int r = r0 + RPW * u + rw;
+            xs[u] = *(const u32x4 *)(dec_row<PAGED>(p, kg, kst, s, kbase, kb + min(r, rows - 1)) + 16 * sub);
+        }
+    };
+    float bmax[GP];
 #pragma unroll
-            for (int u = 0; u < kDecRows; ++u) {
-                const int r = r0 + RPW * u + rw;
-                xs[u] = *(const u32x4 *)(dec_row<PAGED>(p, kg, kst, s, kbase, kb + min(r, rows - 1)) + 16 * sub);
+    for (int h = 0; h < GP; ++h) bmax[h] = -INFINITY;
+    // scores of one batch; after the last batch of a block, the block maximum
+    auto consume = [&](const u32x4 (&xs)[R], int j, int r0) {
+        const int kb = j * p.BK, rows = block_rows(j);
+#pragma unroll
+        for (int u = 0; u < R; ++u) {
+            const int r = r0 + RPW * u + rw;
+            const bool ok = r < rows;
+            bf16x2 kp[NPR];
+            pairs16<F8>(xs[u], kp);
+            float d[GP];
+#pragma unroll
+            for (int h = 0; h < GP; ++h) {
+                d[h] = 0.f;
+#pragma unroll
+                for (int i = 0; i < NPR; ++i) d[h] = __builtin_amdgcn_fdot2_f32_bf16(kp[i], qp[h][i], d[h], false);
+            }
+            row_sums<LPR, GP>(d);
+            float mine = 0.f;  // lane sub < GP stores head sub's score of the row
+#pragma unroll
+            for (int h = 0; h < GP; ++h) {
+                d[h] *= sqk[h];
+                bmax[h] = fmaxf(bmax[h], ok ? d[h] : -INFINITY);
+                mine = sub == h ? d[h] : mine;
+            }
+            if (ok && sub < GP) Sg[(int64_t)(kb + r) * GP + sub] = mine;
+        }
+        if (r0 + RB >= rows) {
+#pragma unroll
+            for (int h = 0; h < GP; ++h) {
+#pragma unroll
+                for (int m = LPR; m < 64; m <<= 1) bmax[h] = fmaxf(bmax[h], __shfl_xor(bmax[h], m));
+            }
+            if (lane < G) {
+                float m = bmax[0];
+#pragma unroll
+                for (int h = 1; h < GP; ++h) m = lane == h ? bmax[h] : m;
+                p.M[((int64_t)(g * G + lane) * p.n_seqs + s) * p.J_max + j] = m;
             }
 #pragma unroll
-            for (int u = 0; u < kDecRows; ++u) {
-                const int r = r0 + RPW * u + rw;
-                const bool ok = r < rows;
-                bf16x2 kp[NPR];
-                pairs16<F8>(xs[u], kp);
-                float d[GP];
-#pragma unroll
-                for (int h = 0; h < GP; ++h) {
-                    d[h] = 0.f;
-#pragma unroll
-                    for (int i = 0; i < NPR; ++i) d[h] = __builtin_amdgcn_fdot2_f32_bf16(kp[i], qp[h][i], d[h], false);
-                }
-                row_sums<LPR, GP>(d);
-                float mine = 0.f;  // lane sub < GP stores head sub's score of the row
-#pragma unroll
-                for (int h = 0; h < GP; ++h) {
-                    d[h] *= sqk[h];
-                    bmax[h] = fmaxf(bmax[h], ok ? d[h] : -INFINITY);
-                    mine = sub == h ? d[h] : mine;
-                }
-                if (ok && sub < GP) Sg[(int64_t)(kb + r) * GP + sub] = mine;
-            }
+            for (int h = 0; h < GP; ++h) bmax[h] = -INFINITY;
         }
-#pragma unroll
-        for (int h = 0; h < GP; ++h) {
-#pragma unroll
-            for (int m = LPR; m < 64; m <<= 1) bmax[h] = fmaxf(bmax[h], __shfl_xor(bmax[h], m));
+    };
+    auto advance = [&](int &j, int &r0) {
+        r0 += RB;
+        if (r0 >= block_rows(j)) {
+            j += 4;
+            r0 = 0;
         }
-        if (lane < G) {
-            float m = bmax[0];
-#pragma unroll
-            for (int h = 1; h < GP; ++h) m = lane == h ? bmax[h] : m;
-            p.M[((int64_t)(g * G + lane) * p.n_seqs + s) * p.J_max + j] = m;
-        }
+    };
+    int j = j0 + w, r0 = 0;
+    u32x4 xa[R], xb[R];
+    if (j < j1) issue(xa, j, 0);
+    while (j < j1) {  // two batches per trip, so that the buffers keep their registers
+        const int ja = j, ra = r0;
+        advance(j, r0);
+        if (j < j1) issue(xb, j, r0);
+        consume(xa, ja, ra);
+        if (j >= j1) break;
+        const int jb = j, rb = r0;
+        advance(j, r0);
+        if (j < j1) issue(xa, j, r0);
+        consume(xb, jb, rb);
     }
 }
 
