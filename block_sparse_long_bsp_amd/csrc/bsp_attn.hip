@@ -852,6 +852,7 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
         // exponentials and row sum. V_j is copied only after a head has decided
         // to keep block j (the V-load skip, below).
         float mloc_a = -INFINITY, mloc_b = -INFINITY;  // row maxima of the block's two key halves
+        int my_vote = 0;  // wave-uniform: this wave's vote on its last QK block
         auto pv_part = [&](int j) {  // PV_{j-1}
             constexpr int PD = kPingPongDepth;
             const char *vbuf = sV[(j - 1) & 1];
@@ -946,6 +947,7 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
                 vote = __all(passes(m_dec, mloc_a)) ? 1 : 0;
             }
             if (lane == 0) sVote[w] = vote;
+            my_vote = vote;
         };
         // Vector phase of block j in sparse mode: the head's decision, then, for a
         // kept block, the reference update, exponentials (in place in the score
@@ -979,13 +981,19 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
         };
         auto v_sparse = [&](int j, auto after_vote) {
             // the votes of this wave's head, or of its half-tile's two waves
-            const int vmask = (KH && p.half_vote != 0) ? 3 << (wq & 2) : (1 << WPH) - 1;
-            int vall = 7;
+            // A wave whose own vote keeps the whole block (both halves under key-half
+            // decisions: the second against the first half kept) knows the decision,
+            // since the head ANDs its waves' skip votes: it reads no vote words.
+            int vall = 0, hk = 1;
+            if ((my_vote & (KH ? 5 : 1)) != 0) {
+                const int vmask = (KH && p.half_vote != 0) ? 3 << (wq & 2) : (1 << WPH) - 1;
+                vall = 7;
 #pragma unroll
-            for (int y = 0; y < WPH; ++y)
-                if ((vmask >> y) & 1) vall &= sVote[hl * WPH + y];
-            const int hk = head_keeps(hl);
-            vall = __builtin_amdgcn_readfirstlane(vall);
+                for (int y = 0; y < WPH; ++y)
+                    if ((vmask >> y) & 1) vall &= sVote[hl * WPH + y];
+                hk = head_keeps(hl);
+                vall = __builtin_amdgcn_readfirstlane(vall);
+            }
             bool ska, skb;  // decisions on the two key halves
             if constexpr (KH) {
                 ska = (vall & 1) != 0;
