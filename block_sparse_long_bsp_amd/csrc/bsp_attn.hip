@@ -1118,8 +1118,9 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
                     // interval 2j: vector phase of block j - 1; K_{j+1}, and V_{j-1} when this head keeps
                     // the block head 0 skipped
                     bool late = false;
+                    const int h0k_lds = sHead;            // read early: its wait falls after the decision
                     v_sparse(j - 1, [&](int hk) {
-                        const int h0k = __builtin_amdgcn_readfirstlane(sHead);
+                        const int h0k = __builtin_amdgcn_readfirstlane(h0k_lds);
 #pragma unroll
                         for (int i = 0; i < CI; ++i) issue_copy(j, i);
                         late = hk != 0 && h0k == 0 && !v_all;
@@ -1136,8 +1137,9 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
                     __syncthreads();
                 }
                 bool late = false;                        // interval 2n: vector phase of block n-1
+                const int h0k_lds = sHead;
                 v_sparse(n - 1, [&](int hk) {
-                    late = hk != 0 && __builtin_amdgcn_readfirstlane(sHead) == 0 && !v_all;
+                    late = hk != 0 && __builtin_amdgcn_readfirstlane(h0k_lds) == 0 && !v_all;
                     if (late) copy_v_head(n - 1);
                 });
                 if (late) {
