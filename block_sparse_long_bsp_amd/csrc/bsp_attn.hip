@@ -847,8 +847,9 @@ __global__ void __launch_bounds__(BQ * 2 * HPW, (BQ == 64 && HPW == 2) ? 2 : 1) 
         // a QK part that also carries the interval's K copies and ends with this
         // wave's vote on block j (causal mask, row max, every valid row's gap to
         // the running max above lambda). The barrier after the matrix phase
-        // publishes the votes; the vector phase reads the head's four votes,
-        // records the decision, and for a kept block runs the reference update,
+        // publishes the votes; the vector phase reads the head's votes (unless
+        // this wave's own vote already keeps the block), records the decision,
+        // and for a kept block runs the reference update,
         // exponentials and row sum. V_j is copied only after a head has decided
         // to keep block j (the V-load skip, below).
         float mloc_a = -INFINITY, mloc_b = -INFINITY;  // row maxima of the block's two key halves
